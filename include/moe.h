@@ -1,0 +1,181 @@
+/*
+ * moe.h -- C ABI of the routed-expert MoE layer for MI355X (gfx950).
+ *
+ * One MoE FFN step of a quantized decode engine: a bf16 router matvec with
+ * top-k softmax per row, the first-seen union of the rows' experts written to
+ * a 64-entry slot table of record descriptors, per union expert an affine
+ * low-bit gate/up matvec fused with silu(gate)*up, the down matvec, and a
+ * routing-weighted combine with a sigmoid-gated shared expert.  The method is
+ * the one the qwen4_exp GPU engine pages describe: "Struct Gpu" (methods
+ * router_b, experts_b, prepare_expert_jobs, pf_experts, encode_block), the
+ * gpu.rs source page (struct Q, struct Moe, MAX_NB, SLOT_STRIDE, union_of, the
+ * slot_tab/wmap field docs) and the gpu/load.rs source page (load_bounded:
+ * shape checks, Moe descriptors, low-bit store kinds).
+ *
+ * Conventions for every entry point
+ *   - Data pointers marked "device" are HIP device memory owned by the caller;
+ *     the library never allocates, frees or keeps them after the call returns.
+ *   - Struct arguments are host memory, read during the call only.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work on it and returns without synchronising.
+ *   - Arguments are validated on the host before any HIP call.  A failed
+ *     check returns MOE_EINVAL or MOE_EWORKSPACE and nothing is enqueued; a
+ *     failed launch returns MOE_ELAUNCH.  moe_last_error() gives the text of
+ *     the last failure on the calling thread.
+ *   - Activations are row-major [rows][...] f32 (the pages' [nb][...] layout).
+ *   - Results are deterministic: no floating-point atomics, fixed summation
+ *     order; two identical calls give identical bits.
+ *
+ * Shapes (checks mirror load.rs load_bounded)
+ *   hidden H      multiple of 256, 256..4096          (hidden % 256 == 0)
+ *   inter  I      power of two, 64..2048              (multiple of the 64-code group)
+ *   n_experts E   1..256
+ *   top_k  k      1..15 and k <= E                    (k * MAX_NB < SLOT_STRIDE)
+ *   nb            1..4 rows per decode step            (MAX_NB = 4)
+ *   t             1..32 rows per prefill chunk
+ *
+ * Record layout (one expert = one record in the byte pool; each section
+ * starts on a 256-byte boundary, in this order):
+ *   GU codes  2I rows x H codes; row 2j = gate row j, row 2j+1 = up row j
+ *   GU sb     2I rows x H/64 words: (scale, bias) bf16 pair per 64-code group
+ *   D codes   H rows x I codes
+ *   D sb      H rows x I/64 words
+ *   An sb word holds the bf16 bits of the scale in its low half and of the
+ *   bias in its high half; w = q * scale + bias.
+ *   Codes, packed into little-endian u32 words, first code in the lowest bits:
+ *     4-bit: 8 per word;  2-bit: 16 per word;
+ *     3-bit: a row is a 2-bit plane of (q & 3) (n/4 bytes) followed by a 1-bit
+ *            plane of (q >> 2) (n/8 bytes); inside each 32-code block, the
+ *            high bit of code i (m = i/16, k = (i/4)%4, p = i%4) is bit
+ *            8k + 4m + p of the block's u32 word.
+ *   Descriptor: u64 = byte offset of the record in the pool (multiple of 256)
+ *   | tag, tag 0 = 4-bit, 1 = 3-bit, 2 = 2-bit (the load.rs low-bit kinds).
+ *   Record bytes: 4-bit 1,769,472 / 3-bit 1,376,256 / 2-bit 983,040 at
+ *   H = 2048, I = 512 (moe_record_bytes).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_MAX_NB 4         /* rows per decode step (gpu.rs MAX_NB) */
+#define MOE_SLOT_STRIDE 64   /* slot table entries per layer (gpu.rs SLOT_STRIDE) */
+#define MOE_RESIDENT_ENTRY 62
+#define MOE_UNION_ENTRY 63
+#define MOE_MAX_PREFILL_ROWS 32
+
+enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,       /* bad shape, count, pointer or alignment */
+    MOE_EWORKSPACE = -2,   /* workspace missing or too small */
+    MOE_ELAUNCH = -3,      /* a kernel launch failed (HIP error text in moe_last_error) */
+};
+
+typedef struct moe_dims {
+    int32_t hidden;      /* H */
+    int32_t inter;       /* I, routed and shared expert width (load.rs requires equal) */
+    int32_t n_experts;   /* E */
+    int32_t top_k;       /* k */
+} moe_dims;
+
+/* One layer's router (gpu.rs Moe.router: the bf16 mlp.gate.weight) and the
+ * descriptors of that layer's routed expert records. */
+typedef struct moe_router {
+    moe_dims dims;
+    const uint16_t *weight;   /* device, bf16 [E][H], 16-byte aligned */
+    const uint64_t *rec;      /* device, [E] record descriptors (u64) */
+} moe_router;
+
+/* The byte pool holding every record. */
+typedef struct moe_pool {
+    const uint8_t *base;      /* device, 256-byte aligned */
+    uint64_t bytes;           /* size of the pool; records must lie inside */
+} moe_pool;
+
+/* The shared expert (load.rs Moe: shared_expert_gate.weight and the shared
+ * gate/up/down projections); always 4-bit ("dense projections stay Q4"). */
+typedef struct moe_shared {
+    const uint16_t *gate;     /* device, bf16 [H] sigmoid gate vector, 16-byte aligned */
+    uint64_t rec;             /* descriptor of its 4-bit record, tag 0 */
+} moe_shared;
+
+/* Routing results of one decode step (device buffers, written by the call). */
+typedef struct moe_slots {
+    uint64_t *tab;        /* [64]: tab[j] = descriptor of union expert j for j < |U|,
+                             0 for |U| <= j < 62, tab[62] = resident count (= |U|:
+                             every record is in device memory), tab[63] = |U| */
+    float    *wmap;       /* [4][64]: routing weight of union slot j in row b, else 0 */
+    uint32_t *ids;        /* [64]: expert id of union slot j (first-seen order), else 0 */
+    uint32_t *topk_idx;   /* [nb][k]: per row, experts by descending logit (ties: lower id) */
+    float    *topk_w;     /* [nb][k]: softmax over the k selected logits */
+    double   *logits;     /* [nb][E]: router logits, f64 accumulation */
+    float    *gamma;      /* [nb]: shared-expert gate sigmoid(gvec . x) */
+    void     *ws;         /* workspace, >= moe_workspace_bytes(dims, nb); must be
+                             zero-filled once after allocation (moe_workspace_init);
+                             every call leaves its counter words zero again */
+    size_t    ws_bytes;
+} moe_slots;
+
+/* Routing results of one prefill chunk, rows grouped by expert (Struct Gpu,
+ * prepare_expert_jobs): experts ascending, rows ascending inside an expert. */
+typedef struct moe_prefill_plan {
+    uint32_t *topk_idx;   /* [t][k] */
+    float    *topk_w;     /* [t][k] */
+    double   *logits;     /* [t][E] */
+    float    *gamma;      /* [t] */
+    int32_t  *expert_ptr; /* [E+1]: rows of expert e are entries ptr[e]..ptr[e+1]-1 */
+    int32_t  *entry_row;  /* [t*k]: row of each entry */
+    int32_t  *entry_rank; /* [t*k]: rank of the expert in that row's top-k */
+    void     *ws;         /* workspace, >= moe_workspace_bytes(dims, t); zero-filled once */
+    size_t    ws_bytes;
+} moe_prefill_plan;
+
+/* Bytes of one record of the given bit width (4, 3 or 2); 0 if invalid. */
+uint64_t moe_record_bytes(int32_t hidden, int32_t inter, int32_t bits);
+
+/* Workspace bytes for up to max_rows rows (1..4 decode, 1..32 prefill);
+ * 0 if dims or max_rows are invalid. */
+size_t moe_workspace_bytes(const moe_dims *dims, int32_t max_rows);
+
+/* Zero-fill a workspace on `stream` (a fill kernel, no memset node). */
+int moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/* Router matvec (f64 accumulation), top-k softmax, union, slot table and
+ * shared-gate value for nb rows of x (device f32 [nb][H], 16-byte aligned).
+ * Struct Gpu router_b + the union publication of service_block, on device. */
+int moe_route(const float *x, int32_t nb, const moe_router *router,
+              const moe_shared *shared, moe_slots *slots, void *stream);
+
+/* The whole layer for nb rows: moe_route, then every union expert and the
+ * shared expert (gate/up + silu*up, down, weighted combine).  out: device f32
+ * [nb][H], 16-byte aligned, overwritten (no residual).  Struct Gpu experts_b. */
+int moe_layer_forward(const float *x, int32_t nb, const moe_router *router,
+                      moe_slots *slots, const moe_pool *pool,
+                      const moe_shared *shared, float *out, void *stream);
+
+/* One prefill chunk of t rows (1..32): route every row, group rows by expert,
+ * run each used expert on its rows with MFMA tiles (8/16/32-row tiles), the
+ * shared expert on all rows, and combine per row in a fixed order.
+ * Struct Gpu prepare_expert_jobs / pf_experts.  out: device f32 [t][H]. */
+int moe_prefill_forward(const float *x, int32_t t, const moe_router *router,
+                        moe_prefill_plan *plan, const moe_pool *pool,
+                        const moe_shared *shared, float *out, void *stream);
+
+/* Status word kept in the workspace: bit 0 set when a kernel met a record
+ * descriptor outside the pool or with tag 3 (that expert was skipped).
+ * Synchronises `stream`, reads the word and clears it; <0 on error. */
+int moe_workspace_status(void *ws, size_t ws_bytes, void *stream);
+
+/* Text of the last non-zero return on the calling thread ("" if none). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -93,7 +93,9 @@ def unpack_codes(packed: np.ndarray, n: int, bits: int) -> np.ndarray:
         low = unpack_codes(packed[:, :low_bytes], n, 2)
         hw = np.ascontiguousarray(packed[:, low_bytes:]).view("<u4")
         hw = hw.reshape(rows, n // 32).astype(np.int64)
-        high = (hw[:, i // 32] >> (i % 32)) & 0x1
+        j = i % 32                      # position inside the 32-code block
+        bit = 8 * ((j // 4) % 4) + 4 * (j // 16) + j % 4
+        high = (hw[:, i // 32] >> bit) & 0x1
         return low + 4 * high
     raise ValueError(f"unsupported bit width {bits}")
 

@@ -1,0 +1,222 @@
+"""Python binding of the routed-expert MoE HIP library (libmoe.so).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  torch is used for device memory and streams; the C ABI itself takes
+plain pointers (see include/moe.h for layouts, ownership and errors).
+Importing this module loads ``libmoe.so`` and raises if it is missing: there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MAX_NB = 4
+SLOT_STRIDE = 64
+RESIDENT_ENTRY = 62
+UNION_ENTRY = 63
+MAX_PREFILL_ROWS = 32
+OK, EINVAL, EWORKSPACE, ELAUNCH = 0, -1, -2, -3
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"moe error {code}: {msg}")
+        self.code = code
+
+
+class MoeDims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32)]
+
+
+class MoeRouter(ctypes.Structure):
+    _fields_ = [("dims", MoeDims), ("weight", ctypes.c_void_p), ("rec", ctypes.c_void_p)]
+
+
+class MoePool(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("bytes", ctypes.c_uint64)]
+
+
+class MoeShared(ctypes.Structure):
+    _fields_ = [("gate", ctypes.c_void_p), ("rec", ctypes.c_uint64)]
+
+
+class MoeSlots(ctypes.Structure):
+    _fields_ = [("tab", ctypes.c_void_p), ("wmap", ctypes.c_void_p), ("ids", ctypes.c_void_p),
+                ("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p),
+                ("logits", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+
+
+class MoePrefillPlan(ctypes.Structure):
+    _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p),
+                ("logits", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("expert_ptr", ctypes.c_void_p), ("entry_row", ctypes.c_void_p),
+                ("entry_rank", ctypes.c_void_p),
+                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m quantized_routed_expert_bf16_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    vp = ctypes.c_void_p
+    lib.moe_record_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    lib.moe_record_bytes.restype = ctypes.c_uint64
+    lib.moe_workspace_bytes.argtypes = [P(MoeDims), ctypes.c_int32]
+    lib.moe_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_workspace_init.argtypes = [vp, ctypes.c_size_t, vp]
+    lib.moe_route.argtypes = [vp, ctypes.c_int32, P(MoeRouter), P(MoeShared), P(MoeSlots), vp]
+    lib.moe_layer_forward.argtypes = [vp, ctypes.c_int32, P(MoeRouter), P(MoeSlots), P(MoePool),
+                                      P(MoeShared), vp, vp]
+    lib.moe_prefill_forward.argtypes = [vp, ctypes.c_int32, P(MoeRouter), P(MoePrefillPlan),
+                                        P(MoePool), P(MoeShared), vp, vp]
+    lib.moe_workspace_status.argtypes = [vp, ctypes.c_size_t, vp]
+    lib.moe_last_error.restype = ctypes.c_char_p
+    for name in ("moe_workspace_init", "moe_route", "moe_layer_forward", "moe_prefill_forward",
+                 "moe_workspace_status"):
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def last_error() -> str:
+    return lib.moe_last_error().decode()
+
+
+def _check(rc: int) -> int:
+    if rc < 0:
+        raise MoeError(rc, last_error())
+    return rc
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ------------------------------------------------------------ plain calls --
+
+def record_bytes(hidden: int, inter: int, bits: int) -> int:
+    return int(lib.moe_record_bytes(hidden, inter, bits))
+
+
+def workspace_bytes(dims: MoeDims, max_rows: int) -> int:
+    return int(lib.moe_workspace_bytes(ctypes.byref(dims), max_rows))
+
+
+def workspace_init(ws: torch.Tensor, stream=None) -> None:
+    _check(lib.moe_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def route(x, nb: int, router: MoeRouter, shared: MoeShared, slots: MoeSlots, stream=None) -> None:
+    _check(lib.moe_route(_ptr(x), nb, ctypes.byref(router), ctypes.byref(shared),
+                         ctypes.byref(slots), _stream(stream)))
+
+
+def layer_forward(x, nb: int, router: MoeRouter, slots: MoeSlots, pool: MoePool,
+                  shared: MoeShared, out, stream=None) -> None:
+    _check(lib.moe_layer_forward(_ptr(x), nb, ctypes.byref(router), ctypes.byref(slots),
+                                 ctypes.byref(pool), ctypes.byref(shared), _ptr(out),
+                                 _stream(stream)))
+
+
+def prefill_forward(x, t: int, router: MoeRouter, plan: MoePrefillPlan, pool: MoePool,
+                    shared: MoeShared, out, stream=None) -> None:
+    _check(lib.moe_prefill_forward(_ptr(x), t, ctypes.byref(router), ctypes.byref(plan),
+                                   ctypes.byref(pool), ctypes.byref(shared), _ptr(out),
+                                   _stream(stream)))
+
+
+def workspace_status(ws: torch.Tensor, stream=None) -> int:
+    return _check(lib.moe_workspace_status(_ptr(ws), ws.numel() * ws.element_size(),
+                                           _stream(stream)))
+
+
+# ------------------------------------------- device buffers (torch plumbing) --
+
+def make_dims(hidden: int, inter: int, n_experts: int, top_k: int) -> MoeDims:
+    return MoeDims(hidden, inter, n_experts, top_k)
+
+
+def make_router(dims: MoeDims, weight: torch.Tensor, rec: torch.Tensor) -> MoeRouter:
+    """weight: bf16 [E][H] on the device; rec: int64 [E] descriptors on the device."""
+    assert weight.dtype == torch.bfloat16 and weight.is_contiguous()
+    assert rec.dtype == torch.int64 and rec.is_contiguous()
+    return MoeRouter(dims, weight.data_ptr(), rec.data_ptr())
+
+
+def make_pool(pool: torch.Tensor) -> MoePool:
+    return MoePool(pool.data_ptr(), pool.numel())
+
+
+def make_shared(gate: torch.Tensor, rec: int) -> MoeShared:
+    assert gate.dtype == torch.bfloat16 and gate.is_contiguous()
+    return MoeShared(gate.data_ptr(), int(rec))
+
+
+class DecodeBuffers:
+    """Device buffers of moe_slots for up to ``max_nb`` rows."""
+
+    def __init__(self, dims: MoeDims, device="cuda", max_nb: int = MAX_NB):
+        E, k = dims.n_experts, dims.top_k
+        dev = torch.device(device)
+        self.tab = torch.zeros(SLOT_STRIDE, dtype=torch.int64, device=dev)
+        self.wmap = torch.zeros(MAX_NB, SLOT_STRIDE, dtype=torch.float32, device=dev)
+        self.ids = torch.zeros(SLOT_STRIDE, dtype=torch.int32, device=dev)
+        self.topk_idx = torch.zeros(max_nb, k, dtype=torch.int32, device=dev)
+        self.topk_w = torch.zeros(max_nb, k, dtype=torch.float32, device=dev)
+        self.logits = torch.zeros(max_nb, E, dtype=torch.float64, device=dev)
+        self.gamma = torch.zeros(max_nb, dtype=torch.float32, device=dev)
+        nbytes = workspace_bytes(dims, max_nb)
+        if nbytes == 0:
+            raise MoeError(EINVAL, "invalid dims")
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        self.slots = MoeSlots(self.tab.data_ptr(), self.wmap.data_ptr(), self.ids.data_ptr(),
+                              self.topk_idx.data_ptr(), self.topk_w.data_ptr(),
+                              self.logits.data_ptr(), self.gamma.data_ptr(),
+                              self.ws.data_ptr(), nbytes)
+
+
+class PrefillBuffers:
+    """Device buffers of moe_prefill_plan for up to ``max_rows`` rows."""
+
+    def __init__(self, dims: MoeDims, device="cuda", max_rows: int = MAX_PREFILL_ROWS):
+        E, k = dims.n_experts, dims.top_k
+        dev = torch.device(device)
+        self.topk_idx = torch.zeros(max_rows, k, dtype=torch.int32, device=dev)
+        self.topk_w = torch.zeros(max_rows, k, dtype=torch.float32, device=dev)
+        self.logits = torch.zeros(max_rows, E, dtype=torch.float64, device=dev)
+        self.gamma = torch.zeros(max_rows, dtype=torch.float32, device=dev)
+        self.expert_ptr = torch.zeros(E + 1, dtype=torch.int32, device=dev)
+        self.entry_row = torch.zeros(max_rows * k, dtype=torch.int32, device=dev)
+        self.entry_rank = torch.zeros(max_rows * k, dtype=torch.int32, device=dev)
+        nbytes = workspace_bytes(dims, max_rows)
+        if nbytes == 0:
+            raise MoeError(EINVAL, "invalid dims")
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        self.plan = MoePrefillPlan(self.topk_idx.data_ptr(), self.topk_w.data_ptr(),
+                                   self.logits.data_ptr(), self.gamma.data_ptr(),
+                                   self.expert_ptr.data_ptr(), self.entry_row.data_ptr(),
+                                   self.entry_rank.data_ptr(), self.ws.data_ptr(), nbytes)

@@ -1,0 +1,315 @@
+// C ABI of the MoE library: host-side validation, workspace layout, launches.
+//
+// The shape checks mirror load.rs load_bounded: hidden % 256 == 0, expert
+// width a multiple of the 64-code group, k * MAX_NB below the 64-entry slot
+// table; the row limits are gpu.rs MAX_NB (decode) and a 32-row prefill tile.
+// Every check runs before the first HIP call, so a rejected call enqueues
+// nothing.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static thread_local char g_err[512] = "";
+
+static int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+static int ok() {
+  g_err[0] = 0;
+  return MOE_OK;
+}
+
+static bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+static bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+static int check_dims(const moe_dims *d) {
+  if (!d) return fail(MOE_EINVAL, "dims is NULL");
+  if (d->hidden < 256 || d->hidden > 4096 || d->hidden % 256)
+    return fail(MOE_EINVAL, "hidden %d: must be a multiple of 256 in 256..4096", d->hidden);
+  if (!pow2(d->inter) || d->inter < 64 || d->inter > 2048)
+    return fail(MOE_EINVAL, "inter %d: expert width must be a power of two in 64..2048 "
+                "(a multiple of the 64-code quantization group)", d->inter);
+  if (d->n_experts < 1 || d->n_experts > kMaxExperts)
+    return fail(MOE_EINVAL, "n_experts %d: must be in 1..%d", d->n_experts, kMaxExperts);
+  if (d->top_k < 1 || d->top_k > kMaxTopK || d->top_k > d->n_experts)
+    return fail(MOE_EINVAL, "top_k %d: must be in 1..%d and <= n_experts (slot table too narrow)",
+                d->top_k, kMaxTopK);
+  return MOE_OK;
+}
+
+#define REQ(p, a, name)                                                              \
+  do {                                                                               \
+    if (!(p)) return fail(MOE_EINVAL, "%s is NULL", name);                           \
+    if (!aligned((p), (a))) return fail(MOE_EINVAL, "%s is not %d-byte aligned", name, int(a)); \
+  } while (0)
+
+WorkspaceLayout workspace_layout(int hidden, int inter, int n_experts, int top_k, int rows) {
+  (void)n_experts;
+  WorkspaceLayout w;
+  size_t pos = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = pos;
+    pos = align256(pos + bytes);
+    return at;
+  };
+  const int pf_rows = rows > MOE_MAX_NB ? rows : MOE_MAX_NB;
+  w.counters = take(256 * sizeof(uint32_t));
+  w.act = take(size_t(kSlotStride) * kMaxNb * inter * sizeof(float));
+  w.ypart = take(size_t(kSlotStride) * kMaxNb * hidden * sizeof(float));
+  w.pf_xh = take(size_t(MOE_MAX_PREFILL_ROWS) * hidden * sizeof(_Float16));
+  w.pf_act = take(size_t(pf_rows) * (top_k + 1) * inter * sizeof(_Float16));
+  w.pf_y = take(size_t(pf_rows) * (top_k + 1) * hidden * sizeof(float));
+  w.total = pos;
+  return w;
+}
+
+static int check_router(const moe_router *r) {
+  if (!r) return fail(MOE_EINVAL, "router is NULL");
+  int rc = check_dims(&r->dims);
+  if (rc) return rc;
+  REQ(r->weight, 16, "router.weight");
+  REQ(r->rec, 8, "router.rec");
+  return MOE_OK;
+}
+
+static int check_shared(const moe_shared *sh, const moe_dims &d, const moe_pool *pool) {
+  if (!sh) return fail(MOE_EINVAL, "shared is NULL");
+  REQ(sh->gate, 16, "shared.gate");
+  if (pool) {
+    if ((sh->rec & 255) != 0)
+      return fail(MOE_EINVAL, "shared.rec: the shared expert must be a 4-bit record (tag 0) "
+                  "at a 256-byte aligned offset");
+    const uint64_t need = record_layout(d.hidden, d.inter, 4).total;
+    if (sh->rec > pool->bytes || pool->bytes - sh->rec < need)
+      return fail(MOE_EINVAL, "shared.rec: record at %llu (+%llu bytes) lies outside the %llu-byte pool",
+                  (unsigned long long)sh->rec, (unsigned long long)need,
+                  (unsigned long long)pool->bytes);
+  }
+  return MOE_OK;
+}
+
+static int check_pool(const moe_pool *p) {
+  if (!p) return fail(MOE_EINVAL, "pool is NULL");
+  REQ(p->base, 256, "pool.base");
+  if (p->bytes == 0) return fail(MOE_EINVAL, "pool.bytes is 0");
+  return MOE_OK;
+}
+
+static int check_ws(void *ws, size_t ws_bytes, const moe_dims &d, int rows) {
+  if (!ws) return fail(MOE_EWORKSPACE, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(MOE_EINVAL, "workspace is not 256-byte aligned");
+  const size_t need = workspace_layout(d.hidden, d.inter, d.n_experts, d.top_k, rows).total;
+  if (ws_bytes < need)
+    return fail(MOE_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  return MOE_OK;
+}
+
+static int launched(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(MOE_ELAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+static int check_slots(const moe_slots *s, const moe_dims &d, int nb) {
+  if (!s) return fail(MOE_EINVAL, "slots is NULL");
+  REQ(s->tab, 8, "slots.tab");
+  REQ(s->wmap, 4, "slots.wmap");
+  REQ(s->ids, 4, "slots.ids");
+  REQ(s->topk_idx, 4, "slots.topk_idx");
+  REQ(s->topk_w, 4, "slots.topk_w");
+  REQ(s->logits, 8, "slots.logits");
+  REQ(s->gamma, 4, "slots.gamma");
+  return check_ws(s->ws, s->ws_bytes, d, nb);
+}
+
+static RouteArgs route_args(const float *x, int rows, const moe_router *r, const moe_shared *sh,
+                            double *logits, float *gamma, uint32_t *topk_idx, float *topk_w,
+                            void *ws) {
+  RouteArgs a{};
+  a.x = x;
+  a.router = r->weight;
+  a.gvec = sh->gate;
+  a.rec = r->rec;
+  a.hidden = r->dims.hidden;
+  a.n_experts = r->dims.n_experts;
+  a.top_k = r->dims.top_k;
+  a.rows = rows;
+  a.logits = logits;
+  a.gamma = gamma;
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.counter = static_cast<uint32_t *>(ws) + kCounterRoute;
+  return a;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+uint64_t moe_record_bytes(int32_t hidden, int32_t inter, int32_t bits) {
+  if (bits != 4 && bits != 3 && bits != 2) return 0;
+  moe_dims d{hidden, inter, 1, 1};
+  if (check_dims(&d)) return 0;
+  return record_layout(hidden, inter, bits).total;
+}
+
+size_t moe_workspace_bytes(const moe_dims *dims, int32_t max_rows) {
+  if (check_dims(dims)) return 0;
+  if (max_rows < 1 || max_rows > MOE_MAX_PREFILL_ROWS) return 0;
+  return workspace_layout(dims->hidden, dims->inter, dims->n_experts, dims->top_k, max_rows).total;
+}
+
+int moe_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+  if (!ws) return fail(MOE_EWORKSPACE, "workspace is NULL");
+  if (!aligned(ws, 256) || ws_bytes % 256)
+    return fail(MOE_EINVAL, "workspace must be 256-byte aligned with a size multiple of 256");
+  const int rc = launched(launch_fill_zero(ws, ws_bytes, static_cast<hipStream_t>(stream)), "fill");
+  return rc ? rc : ok();
+}
+
+int moe_route(const float *x, int32_t nb, const moe_router *router, const moe_shared *shared,
+              moe_slots *slots, void *stream) {
+  int rc = check_router(router);
+  if (rc) return rc;
+  const moe_dims &d = router->dims;
+  if (nb < 1 || nb > MOE_MAX_NB) return fail(MOE_EINVAL, "nb %d: must be in 1..%d", nb, MOE_MAX_NB);
+  REQ(x, 16, "x");
+  if ((rc = check_shared(shared, d, nullptr))) return rc;
+  if ((rc = check_slots(slots, d, nb))) return rc;
+  RouteArgs a = route_args(x, nb, router, shared, slots->logits, slots->gamma, slots->topk_idx,
+                           slots->topk_w, slots->ws);
+  a.tab = slots->tab;
+  a.wmap = slots->wmap;
+  a.ids = slots->ids;
+  rc = launched(launch_route(a, static_cast<hipStream_t>(stream)), "route");
+  return rc ? rc : ok();
+}
+
+int moe_layer_forward(const float *x, int32_t nb, const moe_router *router, moe_slots *slots,
+                      const moe_pool *pool, const moe_shared *shared, float *out, void *stream) {
+  int rc = check_router(router);
+  if (rc) return rc;
+  const moe_dims &d = router->dims;
+  if (nb < 1 || nb > MOE_MAX_NB) return fail(MOE_EINVAL, "nb %d: must be in 1..%d", nb, MOE_MAX_NB);
+  REQ(x, 16, "x");
+  REQ(out, 16, "out");
+  if ((rc = check_pool(pool))) return rc;
+  if ((rc = check_shared(shared, d, pool))) return rc;
+  if ((rc = check_slots(slots, d, nb))) return rc;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RouteArgs ra = route_args(x, nb, router, shared, slots->logits, slots->gamma, slots->topk_idx,
+                            slots->topk_w, slots->ws);
+  ra.tab = slots->tab;
+  ra.wmap = slots->wmap;
+  ra.ids = slots->ids;
+  if ((rc = launched(launch_route(ra, s), "route"))) return rc;
+
+  const WorkspaceLayout L = workspace_layout(d.hidden, d.inter, d.n_experts, d.top_k, nb);
+  uint8_t *ws = static_cast<uint8_t *>(slots->ws);
+  ExpertArgs ea{};
+  ea.pool = pool->base;
+  ea.pool_bytes = pool->bytes;
+  ea.x = x;
+  ea.tab = slots->tab;
+  ea.wmap = slots->wmap;
+  ea.gamma = slots->gamma;
+  ea.shared_rec = shared->rec;
+  ea.hidden = d.hidden;
+  ea.inter = d.inter;
+  ea.act = reinterpret_cast<float *>(ws + L.act);
+  ea.ypart = reinterpret_cast<float *>(ws + L.ypart);
+  ea.tile_count = reinterpret_cast<uint32_t *>(ws + L.counters) + kCounterTiles;
+  ea.status = reinterpret_cast<uint32_t *>(ws + L.counters) + kCounterStatus;
+  ea.out = out;
+  const int max_slots = d.top_k * nb + 1;
+  if ((rc = launched(launch_gate_up(ea, nb, max_slots, s), "gate_up"))) return rc;
+  if ((rc = launched(launch_down(ea, nb, max_slots, s), "down"))) return rc;
+  return ok();
+}
+
+int moe_prefill_forward(const float *x, int32_t t, const moe_router *router, moe_prefill_plan *plan,
+                        const moe_pool *pool, const moe_shared *shared, float *out, void *stream) {
+  int rc = check_router(router);
+  if (rc) return rc;
+  const moe_dims &d = router->dims;
+  if (t < 1 || t > MOE_MAX_PREFILL_ROWS)
+    return fail(MOE_EINVAL, "t %d: must be in 1..%d", t, MOE_MAX_PREFILL_ROWS);
+  REQ(x, 16, "x");
+  REQ(out, 16, "out");
+  if ((rc = check_pool(pool))) return rc;
+  if ((rc = check_shared(shared, d, pool))) return rc;
+  if (!plan) return fail(MOE_EINVAL, "plan is NULL");
+  REQ(plan->topk_idx, 4, "plan.topk_idx");
+  REQ(plan->topk_w, 4, "plan.topk_w");
+  REQ(plan->logits, 8, "plan.logits");
+  REQ(plan->gamma, 4, "plan.gamma");
+  REQ(plan->expert_ptr, 4, "plan.expert_ptr");
+  REQ(plan->entry_row, 4, "plan.entry_row");
+  REQ(plan->entry_rank, 4, "plan.entry_rank");
+  if ((rc = check_ws(plan->ws, plan->ws_bytes, d, t))) return rc;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RouteArgs ra = route_args(x, t, router, shared, plan->logits, plan->gamma, plan->topk_idx,
+                            plan->topk_w, plan->ws);
+  ra.expert_ptr = plan->expert_ptr;
+  ra.entry_row = plan->entry_row;
+  ra.entry_rank = plan->entry_rank;
+  if ((rc = launched(launch_prefill_route(ra, s), "prefill route"))) return rc;
+
+  const WorkspaceLayout L = workspace_layout(d.hidden, d.inter, d.n_experts, d.top_k, t);
+  uint8_t *ws = static_cast<uint8_t *>(plan->ws);
+  PrefillArgs pa{};
+  pa.pool = pool->base;
+  pa.pool_bytes = pool->bytes;
+  pa.x = x;
+  pa.rec = router->rec;
+  pa.shared_rec = shared->rec;
+  pa.expert_ptr = plan->expert_ptr;
+  pa.entry_row = plan->entry_row;
+  pa.entry_rank = plan->entry_rank;
+  pa.topk_w = plan->topk_w;
+  pa.gamma = plan->gamma;
+  pa.hidden = d.hidden;
+  pa.inter = d.inter;
+  pa.n_experts = d.n_experts;
+  pa.top_k = d.top_k;
+  pa.t = t;
+  pa.xh = reinterpret_cast<_Float16 *>(ws + L.pf_xh);
+  pa.act = reinterpret_cast<_Float16 *>(ws + L.pf_act);
+  pa.y = reinterpret_cast<float *>(ws + L.pf_y);
+  pa.status = reinterpret_cast<uint32_t *>(ws + L.counters) + kCounterStatus;
+  pa.out = out;
+  if ((rc = launched(launch_prefill_experts(pa, s), "prefill experts"))) return rc;
+  return ok();
+}
+
+int moe_workspace_status(void *ws, size_t ws_bytes, void *stream) {
+  if (!ws || ws_bytes < 256 * sizeof(uint32_t)) return fail(MOE_EWORKSPACE, "workspace is NULL or too small");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t *word = static_cast<uint32_t *>(ws) + kCounterStatus;
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, word, sizeof v, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  const uint32_t zero = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(word, &zero, sizeof zero, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(MOE_ELAUNCH, "status read failed: %s", hipGetErrorString(e));
+  ok();
+  return int(v & 0x7fffffff);
+}
+
+const char *moe_last_error(void) { return g_err; }
+
+}  // extern "C"

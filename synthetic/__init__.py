@@ -20,8 +20,9 @@ Code packing inside a row (little-endian u32 words):
   4-bit: code i is bits [4*(i%8), 4*(i%8)+4) of word i//8.
   2-bit: code i is bits [2*(i%16), 2*(i%16)+2) of word i//16.
   3-bit: the row is two planes: first the low two bits of every code packed
-         exactly like a 2-bit row (n/4 bytes), then the high bit of every code,
-         bit i%32 of word i//32 (n/8 bytes).
+         exactly like a 2-bit row (n/4 bytes), then the high bits (n/8 bytes),
+         one u32 word per 32-code block; code i of a block (m = i//16,
+         k = (i//4)%4, p = i%4) has its high bit at bit 8k + 4m + p.
 An (s, b) pair is one u32 word: bf16 bits of s in the low half, of b in the
 high half.  A record descriptor is ``byte_offset | tag`` with the offset a
 multiple of 256 and tag 0/1/2 for 4/3/2-bit codes.
@@ -94,7 +95,9 @@ def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
     if bits == 3:
         low = pack_codes(codes & 3, 2)
         hb = (codes >> 2).reshape(rows, n // 32, 32)
-        words = (hb << np.arange(32, dtype=np.uint64)).sum(axis=2).astype(np.uint32)
+        i = np.arange(32, dtype=np.uint64)
+        pos = 8 * ((i // 4) % 4) + 4 * (i // 16) + i % 4
+        words = (hb << pos).sum(axis=2).astype(np.uint32)
         high = words.view(np.uint8).reshape(rows, -1)
         return np.concatenate([low, high], axis=1)
     raise ValueError(bits)

@@ -1,0 +1,142 @@
+"""GPU parity of the decode path (moe_route / moe_layer_forward) against the
+CPU oracle, through the C ABI, on seeded synthetic inputs."""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_oracle as mo
+import synthetic as syn
+from gpu_support import (DecodeRunner, PoolView, compare_decode, oracle_layer, problem_to, u16)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_routed_expert_bf16_amd as m
+    return m
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _x(cfg, seed, nb, H, device):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(nb, H, generator=g)
+    if cfg.x_mode == "correlated":
+        x = x[:1] + 0.3 * torch.cat([torch.zeros(1, H), x[1:]])
+    x = x / torch.sqrt((x * x).mean(dim=1, keepdim=True))
+    return x.to(device).contiguous()
+
+
+def _small_cfg(**kw):
+    base = syn.CONFIGS["tiny"]
+    return dataclasses.replace(base, name="custom", **kw)
+
+
+@pytest.mark.parametrize("nb", [1, 2, 3, 4])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_layer(moe, nb, seed):
+    cfg = syn.CONFIGS["tiny"]
+    _say(f"[tiny] seed={seed} nb={nb}")
+    p = problem_to(syn.make_problem(cfg, seed=seed, device="cpu"), "cuda")
+    run = DecodeRunner(moe, p)
+    x = _x(cfg, seed, nb, cfg.hidden, "cuda")
+    g = run.forward(x, 0)
+    r = oracle_layer(p, x.cpu().numpy(), 0)
+    st = compare_decode(g, r, cfg.top_k, f"tiny seed {seed} nb {nb}")
+    assert st["ambiguous"] == 0
+    assert moe.workspace_status(run.bufs.ws) == 0
+
+
+@pytest.mark.parametrize("shape", [
+    dict(hidden=256, inter=64, n_experts=4, top_k=1),        # smallest width
+    dict(hidden=512, inter=2048, n_experts=3, top_k=3),      # widest expert, k = E
+    dict(hidden=4096, inter=256, n_experts=16, top_k=4),     # two chunks per lane
+    dict(hidden=768, inter=128, n_experts=1, top_k=1),       # single expert
+    dict(hidden=256, inter=128, n_experts=256, top_k=15),    # max experts and k
+])
+@pytest.mark.parametrize("bits", ["q4", "q3", "q2", "mixed"])
+def test_shapes_and_bits(moe, shape, bits):
+    cfg = _small_cfg(bits=bits, x_mode="correlated", **shape)
+    _say(f"[shape] {shape} {bits}")
+    p = problem_to(syn.make_problem(cfg, seed=5, device="cpu"), "cuda")
+    run = DecodeRunner(moe, p)
+    for nb in (1, 4):
+        x = _x(cfg, 11 + nb, nb, cfg.hidden, "cuda")
+        g = run.forward(x, 0)
+        r = oracle_layer(p, x.cpu().numpy(), 0)
+        compare_decode(g, r, cfg.top_k, f"{shape} {bits} nb {nb}")
+    assert moe.workspace_status(run.bufs.ws) == 0
+
+
+@pytest.mark.parametrize("name,nb", [("decode_nb1", 1), ("verify_nb4", 4), ("lowbit_q3", 4),
+                                     ("lowbit_q2", 4), ("mixed_q4q2", 4)])
+def test_full_shape_layers(moe, name, nb):
+    """H 2048, I 512, 128 experts, top-8, two layers generated on the device."""
+    cfg = syn.CONFIGS[name]
+    _say(f"[full-shape] {name}")
+    p = syn.make_problem(cfg, seed=1, device="cuda", n_layers=2)
+    run = DecodeRunner(moe, p)
+    xs = syn.make_x(cfg, seed=3, steps=2, device="cuda", problem=p)
+    for step in range(2):
+        for layer in range(2):
+            x = xs[step, layer]
+            g = run.forward(x, layer)
+            r = oracle_layer(p, x.cpu().numpy(), layer)
+            st = compare_decode(g, r, cfg.top_k, f"{name} step {step} layer {layer}")
+            _say(f"   step {step} layer {layer}: |U|={st['union']} rel err {st['rel']:.2e}")
+    assert moe.workspace_status(run.bufs.ws) == 0
+
+
+def test_route_only_matches_forward(moe):
+    cfg = syn.CONFIGS["verify_nb4"]
+    p = syn.make_problem(cfg, seed=2, device="cuda", n_layers=1)
+    run = DecodeRunner(moe, p)
+    x = syn.make_x(cfg, seed=9, steps=1, device="cuda", problem=p)[0, 0]
+    a = run.route(x, 0)
+    b = run.forward(x, 0)
+    for key in ("tab", "wmap", "ids", "topk_idx", "topk_w", "logits", "gamma"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+
+
+def test_deterministic_repeat(moe):
+    cfg = syn.CONFIGS["verify_nb4"]
+    p = syn.make_problem(cfg, seed=4, device="cuda", n_layers=1)
+    run = DecodeRunner(moe, p)
+    x = syn.make_x(cfg, seed=4, steps=1, device="cuda", problem=p)[0, 0]
+    first = run.forward(x, 0)
+    for _ in range(5):
+        again = run.forward(x, 0)
+        for key in first:
+            np.testing.assert_array_equal(first[key], again[key], err_msg=key)
+
+
+def test_bad_descriptor_is_skipped_and_flagged(moe):
+    """A routed record descriptor that points past the pool: the kernels skip
+    that expert (in-bounds check), flag the workspace status word, and the
+    other experts still match the oracle with that expert's weight dropped."""
+    cfg = syn.CONFIGS["tiny"]
+    p = problem_to(syn.make_problem(cfg, seed=0, device="cpu"), "cuda")
+    x = _x(cfg, 0, 1, cfg.hidden, "cuda")
+    r = oracle_layer(p, x.cpu().numpy(), 0)
+    bad_e = int(r["topk_idx"][0, 0])
+    rec = p.rec.clone()
+    rec[0, bad_e] = (p.pool.numel() + 4096) & ~0xFF
+    p2 = dataclasses.replace(p, rec=rec)
+    run = DecodeRunner(moe, p2)
+    g = run.forward(x, 0)
+    assert moe.workspace_status(run.bufs.ws) & 1
+    # expected: the oracle's output minus the skipped expert's weighted output
+    Wg, Wu, Wd = mo.read_expert(PoolView(p.pool), int(p.rec[0, bad_e]), cfg.hidden, cfg.inter)
+    y, _ = mo.expert_mlp(Wg, Wu, Wd, x.cpu().numpy()[0].astype(np.float64))
+    expect = r["out_f64"][0] - r["topk_w"][0, 0] * y
+    err = np.abs(g["out"][0] - expect).max()
+    assert err <= 1e-3 * np.abs(expect).max()
+    assert moe.workspace_status(run.bufs.ws) == 0     # read-and-clear

@@ -87,7 +87,7 @@ def test_unpack_matches_golden_words():
             np.testing.assert_array_equal(syn.pack_codes(codes[None, :], bits)[0],
                                           words.view(np.uint8))
             n_cases += 1
-    assert n_cases == 8
+    assert n_cases == 9
 
 
 @pytest.mark.parametrize("bits", [4, 3, 2])
