@@ -1,0 +1,430 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--extra a,b] [--mode graph|eager]
+
+A step is one pass of the whole hot path over one batch: the 40 MoE layers of
+the workload (route, union/slot table, gate/up + silu*up, down + combine with
+the shared expert), each layer with its own fresh synthetic activations.
+Inputs are generated on the device and resident in HBM before timing starts.
+
+Printed: ONE JSON line.  ``value`` is the expert-weight bandwidth of the main
+configuration (algorithmic bytes of the union records plus the shared record,
+with |U| as measured per layer, divided by wall time on the device), in GB/s;
+``us_per_layer`` and the fraction of the 8 TB/s HBM peak ride along.
+``roofline`` describes the dominant kernel (the fused gate/up kernel), timed
+with HIP events on the launch stream; ``cpu_baseline`` times the float64 CPU
+oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD public figure
+METRIC = "µs per MoE layer and expert-weight GB/s (% HBM peak) at nb=1,4"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="decode_nb1")
+    ap.add_argument("--extra", default="verify_nb4",
+                    help="comma-separated further configurations reported under 'extra'")
+    ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
+    ap.add_argument("--chunk", type=int, default=25, help="steps per captured graph")
+    ap.add_argument("--stage-steps", type=int, default=100)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+class DecodeBench:
+    def __init__(self, moe, torch, syn, cfg, steps, warmup, seed):
+        self.moe, self.torch, self.syn, self.cfg = moe, torch, syn, cfg
+        self.steps, self.warmup = steps, warmup
+        t0 = time.time()
+        self.p = syn.make_problem(cfg, seed=seed, device="cuda")
+        self.x = syn.make_x(cfg, seed=seed + 1, steps=steps + warmup, device="cuda", problem=self.p)
+        torch.cuda.synchronize()
+        log(f"{cfg.name}: pool {self.p.pool.numel() / 2**30:.2f} GiB generated in {time.time() - t0:.1f} s")
+        c = cfg
+        self.L = self.p.rec.shape[0]
+        self.nb = c.nb
+        self.dims = moe.make_dims(c.hidden, c.inter, c.n_experts, c.top_k)
+        self.bufs = moe.DecodeBuffers(self.dims)
+        self.pool = moe.make_pool(self.p.pool)
+        self.routers = [moe.make_router(self.dims, self.p.router[l], self.p.rec[l]) for l in range(self.L)]
+        self.shared = [moe.make_shared(self.p.shared_gate[l], int(self.p.shared_rec[l]))
+                       for l in range(self.L)]
+        self.out = torch.zeros(self.L, self.nb, c.hidden, dtype=torch.float32, device="cuda")
+        import ctypes
+        self.ct = ctypes
+        self.f = moe.lib.moe_layer_forward
+        self.ref = {"slots": ctypes.byref(self.bufs.slots), "pool": ctypes.byref(self.pool),
+                    "routers": [ctypes.byref(r) for r in self.routers],
+                    "shared": [ctypes.byref(s) for s in self.shared]}
+        self.x_ptr = self.x.data_ptr()
+        self.x_step = self.x[0].numel() * 4
+        self.x_layer = self.x[0, 0].numel() * 4
+        self.out_ptr = [self.out[l].data_ptr() for l in range(self.L)]
+
+    # one step (all layers) of the layer call, on the current stream
+    def step(self, s: int, stream: int):
+        ref = self.ref
+        base = self.x_ptr + s * self.x_step
+        for l in range(self.L):
+            rc = self.f(base + l * self.x_layer, self.nb, ref["routers"][l], ref["slots"], ref["pool"],
+                        ref["shared"][l], self.out_ptr[l], stream)
+            if rc:
+                raise self.moe.MoeError(rc, self.moe.last_error())
+
+    def stream(self) -> int:
+        return self.torch.cuda.current_stream().cuda_stream
+
+    def union_pass(self):
+        """Slot tables of every timed (step, layer): route-only calls, tab copied on device."""
+        torch = self.torch
+        tabs = torch.zeros(self.steps, self.L, 64, dtype=torch.int64, device="cuda")
+        st = self.stream()
+        for s in range(self.steps):
+            base = self.x_ptr + (self.warmup + s) * self.x_step
+            for l in range(self.L):
+                self.moe.lib.moe_route(base + l * self.x_layer, self.nb, self.ref["routers"][l],
+                                       self.ct.byref(self.shared[l]), self.ref["slots"], st)
+                tabs[s, l].copy_(self.bufs.tab)
+        torch.cuda.synchronize()
+        return tabs.cpu().numpy()
+
+    def bytes_of(self, tabs):
+        """Algorithmic bytes per (step, layer): expert records, and everything."""
+        import numpy as np
+        c, moe = self.cfg, self.moe
+        rb = {tag: moe.record_bytes(c.hidden, c.inter, bits) for tag, bits in ((0, 4), (1, 3), (2, 2))}
+        gu = {}
+        for tag, bits in ((0, 4), (1, 3), (2, 2)):
+            gu[tag] = 2 * c.inter * (c.hidden * bits // 8) + 2 * c.inter * (c.hidden // 64) * 4
+        u = tabs[:, :, 63].astype(np.int64)
+        expert = np.zeros(u.shape, dtype=np.float64)
+        gu_bytes = np.zeros(u.shape, dtype=np.float64)
+        for s in range(u.shape[0]):
+            for l in range(u.shape[1]):
+                tags = tabs[s, l, : u[s, l]] & 3
+                expert[s, l] = sum(rb[int(t)] for t in tags) + rb[0]
+                gu_bytes[s, l] = sum(gu[int(t)] for t in tags) + gu[0]
+        other = c.n_experts * c.hidden * 2 + c.hidden * 2 + 2 * self.nb * c.hidden * 4
+        # gate/up kernel: GU sections + x in + act out
+        gu_kernel = gu_bytes + self.nb * c.hidden * 4 + (u + 1) * self.nb * c.inter * 4
+        return u, expert, expert + other, gu_kernel
+
+    def run_eager(self):
+        torch = self.torch
+        st = self.stream()
+        for s in range(self.warmup):
+            self.step(s, st)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(self.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(self.steps):
+            evs[i][0].record()
+            self.step(self.warmup + i, st)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per_step = [a.elapsed_time(b) for a, b in evs]
+        return per_step, 1, wall
+
+    def run_graph(self, chunk):
+        torch = self.torch
+        n_chunks = (self.steps + chunk - 1) // chunk
+        graphs = []
+        st_side = torch.cuda.Stream()
+        # warm-up steps eagerly (clocks, code objects), then capture
+        self.step(0, self.stream())
+        torch.cuda.synchronize()
+        wg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(wg, stream=st_side):
+            for s in range(self.warmup):
+                self.step(s, torch.cuda.current_stream().cuda_stream)
+        for c in range(n_chunks):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=st_side):
+                sc = torch.cuda.current_stream().cuda_stream
+                for s in range(c * chunk, min(self.steps, (c + 1) * chunk)):
+                    self.step(self.warmup + s, sc)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            wg.replay()
+        for g in graphs:           # first replays upload the graphs
+            g.replay()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in graphs]
+        t0 = time.perf_counter()
+        for g, (a, b) in zip(graphs, evs):
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per_chunk = [a.elapsed_time(b) for a, b in evs]
+        sizes = [min(self.steps, (c + 1) * chunk) - c * chunk for c in range(n_chunks)]
+        per_step = [t / n for t, n in zip(per_chunk, sizes)]
+        return per_step, chunk, wall, sum(per_chunk)
+
+    def stage_pass(self, n_steps):
+        """Per-kernel durations from HIP events recorded between the layer's kernels."""
+        torch, moe = self.torch, self.moe
+        n_steps = min(n_steps, self.steps)
+        n = n_steps * self.L
+        ev = HipEvents(2 * n)
+        arr_t = self.ct.c_void_p * 1
+        st = self.stream()
+        i = 0
+        for s in range(n_steps):
+            base = self.x_ptr + (self.warmup + s) * self.x_step
+            for l in range(self.L):
+                arr = arr_t(ev.ev[2 * i + 1])
+                rc = moe.lib.moe_set_stage_events(arr, 1)
+                if rc:
+                    raise moe.MoeError(rc, moe.last_error())
+                ev.record(2 * i, st)
+                rc = self.f(base + l * self.x_layer, self.nb, self.ref["routers"][l], self.ref["slots"],
+                            self.ref["pool"], self.ref["shared"][l], self.out_ptr[l], st)
+                if rc:
+                    raise moe.MoeError(rc, moe.last_error())
+                i += 1
+        moe.lib.moe_set_stage_events(None, 0)
+        torch.cuda.synchronize()
+        layer = [ev.ms(2 * i, 2 * i + 1) * 1e3 for i in range(n)]
+        ev.close()
+        return n_steps, layer
+
+    def snapshot_layers(self, step, layers):
+        """GPU outputs and slot tables of one step's first layers (for parity)."""
+        torch = self.torch
+        res = []
+        st = self.stream()
+        base = self.x_ptr + (self.warmup + step) * self.x_step
+        for l in range(layers):
+            rc = self.f(base + l * self.x_layer, self.nb, self.ref["routers"][l], self.ref["slots"],
+                        self.ref["pool"], self.ref["shared"][l], self.out_ptr[l], st)
+            if rc:
+                raise self.moe.MoeError(rc, self.moe.last_error())
+            torch.cuda.synchronize()
+            res.append({"out": self.out[l].cpu().numpy().copy(),
+                        "ids": self.bufs.ids.cpu().numpy().copy(),
+                        "tab": self.bufs.tab.cpu().numpy().copy()})
+        return res
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (created eagerly, unlike torch's lazy events), so
+    the library's stage hook can record them; read back with
+    hipEventElapsedTime."""
+
+    def __init__(self, n: int):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(h))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            self.ev.append(h.value)
+
+    def record(self, i: int, stream: int):
+        rc = self.hip.hipEventRecord(self.ev[i], stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def ms(self, i: int, j: int) -> float:
+        out = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(out), self.ev[i], self.ev[j])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return out.value
+
+    def close(self):
+        for h in self.ev:
+            self.hip.hipEventDestroy(h)
+        self.ev = []
+
+
+def pct(v, q):
+    v = sorted(v)
+    return v[min(len(v) - 1, int(q * (len(v) - 1) + 0.5))]
+
+
+def bench_decode(moe, torch, syn, name, args, with_cpu):
+    import numpy as np
+    cfg = syn.CONFIGS[name]
+    b = DecodeBench(moe, torch, syn, cfg, args.steps, args.warmup, args.seed)
+    log(f"{name}: union pass")
+    tabs = b.union_pass()
+    u, expert_b, all_b, _ = b.bytes_of(tabs)
+    log(f"{name}: timed pass ({args.mode})")
+    if args.mode == "graph":
+        per_step, _, wall, total_ms = b.run_graph(args.chunk)
+    else:
+        per_step, _, wall = b.run_eager()
+        total_ms = sum(per_step)
+    L = b.L
+    us_layer = [t * 1e3 / L for t in per_step]
+    total_s = total_ms / 1e3
+    expert_gbs = expert_b.sum() / total_s / 1e9
+    all_gbs = all_b.sum() / total_s / 1e9
+    log(f"{name}: {statistics.median(us_layer):.2f} us/layer, expert {expert_gbs:.0f} GB/s")
+    log(f"{name}: stage pass")
+    n_st, layer_us = b.stage_pass(args.stage_steps)
+    k_us = statistics.mean(layer_us)
+    k_bytes = all_b[:n_st].reshape(-1)
+    k_gbs = float(np.mean(k_bytes)) / (k_us * 1e-6) / 1e9
+    out = {
+        "config": name,
+        "description": cfg.description,
+        "nb": cfg.nb, "layers": L, "steps": args.steps, "mode": args.mode,
+        "us_per_layer_median": statistics.median(us_layer),
+        "us_per_layer_p90": pct(us_layer, 0.9),
+        "us_per_layer_mean": total_ms * 1e3 / (L * args.steps),
+        "ms_per_step": total_ms / args.steps,
+        "expert_weight_gbs": expert_gbs,
+        "expert_weight_hbm_frac": expert_gbs / HBM_PEAK_GBS,
+        "all_bytes_gbs": all_gbs,
+        "expert_bytes_per_layer_mean": float(expert_b.mean()),
+        "union_mean": float(u.mean()), "union_min": int(u.min()), "union_max": int(u.max()),
+        "kernel_us_mean": k_us,
+        "kernel_us_median": statistics.median(layer_us),
+        "stage_steps": n_st,
+        "kernel_bytes_per_launch_mean": float(np.mean(k_bytes)),
+        "kernel_gbs": k_gbs,
+        "wall_s": wall,
+    }
+    if with_cpu:
+        out["cpu"] = cpu_baseline(b, args.cpu_seconds)
+    del b
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(b, seconds):
+    """The float64 oracle on the host, on the first layers of the first timed step."""
+    import numpy as np
+    import oracle.moe_oracle as mo
+    c = b.cfg
+    log(f"cpu baseline: copying the pool to the host")
+    pool = b.p.pool.cpu().numpy()
+    routers = b.p.router.view(b.torch.int16).cpu().numpy().view(np.uint16)
+    gates = b.p.shared_gate.view(b.torch.int16).cpu().numpy().view(np.uint16)
+    rec = b.p.rec.cpu().numpy()
+    srec = b.p.shared_rec.cpu().numpy()
+    x = b.x[b.warmup].cpu().numpy()
+    threads = None
+    try:
+        import threadpoolctl
+        threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    except Exception:
+        threads = 1
+    gpu = None
+    t_total = 0.0
+    n = 0
+    refs = []
+    while n < b.L and (t_total < seconds or n == 0):
+        t0 = time.perf_counter()
+        r = mo.layer_forward(x[n], routers[n], rec[n], pool, gates[n], int(srec[n]), c.top_k,
+                             c.hidden, c.inter)
+        t_total += time.perf_counter() - t0
+        refs.append(r)
+        n += 1
+    gpu = b.snapshot_layers(0, n)
+    # parity of the sampled layers (same seeded inputs)
+    rel, ids_exact = 0.0, True
+    expert_bytes = 0
+    for r, g in zip(refs, gpu):
+        ref = r["out_f64"]
+        rel = max(rel, float(np.abs(g["out"] - ref).max() / np.abs(ref).max()))
+        ids_exact &= bool(np.array_equal(g["ids"].view(np.uint32), r["ids"]))
+        u = r["n_union"]
+        expert_bytes += sum(b.moe.record_bytes(c.hidden, c.inter, {0: 4, 1: 3, 2: 2}[int(d) & 3])
+                            for d in r["tab"][:u]) + b.moe.record_bytes(c.hidden, c.inter, 4)
+    log(f"cpu baseline: {n} layers in {t_total:.1f} s; parity max rel err {rel:.2e} ids exact {ids_exact}")
+    return {"value": expert_bytes / t_total / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "us_per_layer": t_total / n * 1e6,
+            "sample": f"{c.name}: first {n} layers of timed step 0 (same seeded inputs), "
+                      f"float64 numpy oracle, host pool copy excluded",
+            "parity_sampled": {"layers": n, "max_err_over_absmax": rel, "ids_exact": ids_exact}}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(expert-parallel sharding is a design note, not built)"}))
+        sys.exit(2)
+    import torch
+    import quantized_routed_expert_bf16_amd as moe
+    import synthetic as syn
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    main_res = bench_decode(moe, torch, syn, args.config, args, with_cpu=not args.no_cpu)
+    extra = {}
+    for name in [n for n in args.extra.split(",") if n]:
+        extra[name] = bench_decode(moe, torch, syn, name, args, with_cpu=False)
+    line = {
+        "metric": METRIC,
+        "value": round(main_res["expert_weight_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{main_res['config']}: {main_res['description']}, "
+                               f"{main_res['layers']} layers, fresh x per layer",
+                   "nb": main_res["nb"], "layers": main_res["layers"], "mode": args.mode},
+        "us_per_layer": round(main_res["us_per_layer_median"], 3),
+        "us_per_layer_p90": round(main_res["us_per_layer_p90"], 3),
+        "hbm_frac": round(main_res["expert_weight_hbm_frac"], 4),
+        "roofline": {"bound": "hbm", "kernel": "layer_kernel (the fused decode layer)",
+                     "achieved": round(main_res["kernel_gbs"], 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(main_res["kernel_gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "bytes_per_launch": round(main_res["kernel_bytes_per_launch_mean"]),
+                     "us_per_launch": round(main_res["kernel_us_mean"], 3)},
+        "cpu_baseline": main_res.get("cpu"),
+        "detail": main_res,
+        "extra": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -38,8 +38,9 @@
  * starts on a 256-byte boundary, in this order):
  *   GU codes  2I rows x H codes; row 2j = gate row j, row 2j+1 = up row j
  *   GU sb     2I rows x H/64 words: (scale, bias) bf16 pair per 64-code group
- *   D codes   H rows x I codes
- *   D sb      H rows x I/64 words
+ *   D codes   group-major: I/64 column groups, each H rows, each row's 64
+ *             codes of that group packed like a 64-code row
+ *   D sb      group-major: I/64 column groups, each H words
  *   An sb word holds the bf16 bits of the scale in its low half and of the
  *   bias in its high half; w = q * scale + bias.
  *   Codes, packed into little-endian u32 words, first code in the lowest bits:
@@ -170,6 +171,14 @@ int moe_prefill_forward(const float *x, int32_t t, const moe_router *router,
  * descriptor outside the pool or with tag 3 (that expert was skipped).
  * Synchronises `stream`, reads the word and clears it; <0 on error. */
 int moe_workspace_status(void *ws, size_t ws_bytes, void *stream);
+
+/* Profiling hook (the analog of per-phase GPU timestamps): for the calling
+ * thread, moe_layer_forward records events[i] (hipEvent_t, created by the
+ * caller) on its stream right after its i-th kernel -- 0: route, 1: gate/up,
+ * 2: down/combine -- and moe_prefill_forward after its own kernels in order.
+ * Entries may be NULL; n = 0 turns the hook off.  No work is skipped.  At
+ * most 8 events. */
+int moe_set_stage_events(void *const *events, int32_t n);
 
 /* Text of the last non-zero return on the calling thread ("" if none). */
 const char *moe_last_error(void);

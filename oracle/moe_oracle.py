@@ -60,8 +60,9 @@ def _round_up(n: int, a: int) -> int:
 
 def record_layout(hidden: int, inter: int, bits: int) -> dict:
     """Section offsets of one record, read from the record format: gate/up
-    codes (2I rows of H codes), their (s,b) words, down codes (H rows of I
-    codes), their (s,b) words; each section 256-byte aligned."""
+    codes (2I rows of H codes), their (s,b) words, down codes (I/64 column
+    groups of H rows of 64 codes), their (s,b) words (group-major too); each
+    section 256-byte aligned."""
     sizes = [
         ("gu_codes", 2 * inter * hidden * bits // 8),
         ("gu_sb", 2 * inter * (hidden // GROUP) * 4),
@@ -131,8 +132,11 @@ def read_expert(pool, desc: int, hidden: int, inter: int):
 
     gu_q = unpack_codes(sect("gu_codes").reshape(2 * inter, -1), hidden, bits)
     gu_sb = sect("gu_sb").view("<u4").reshape(2 * inter, hidden // GROUP)
-    d_q = unpack_codes(sect("d_codes").reshape(hidden, -1), inter, bits)
-    d_sb = sect("d_sb").view("<u4").reshape(hidden, inter // GROUP)
+    n_groups = inter // GROUP
+    # down codes are stored group-major: [group][row][64 codes]
+    d_grouped = unpack_codes(sect("d_codes").reshape(n_groups * hidden, -1), GROUP, bits)
+    d_q = d_grouped.reshape(n_groups, hidden, GROUP).transpose(1, 0, 2).reshape(hidden, inter)
+    d_sb = sect("d_sb").view("<u4").reshape(n_groups, hidden).T
     gu = dequant(gu_q, gu_sb)
     return gu[0::2], gu[1::2], dequant(d_q, d_sb)
 

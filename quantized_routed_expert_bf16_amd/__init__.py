@@ -65,7 +65,7 @@ class MoePrefillPlan(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m quantized_routed_expert_bf16_amd.build`")
+                          "`python quantized_routed_expert_bf16_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     vp = ctypes.c_void_p
@@ -80,8 +80,9 @@ def _load():
     lib.moe_prefill_forward.argtypes = [vp, ctypes.c_int32, P(MoeRouter), P(MoePrefillPlan),
                                         P(MoePool), P(MoeShared), vp, vp]
     lib.moe_workspace_status.argtypes = [vp, ctypes.c_size_t, vp]
+    lib.moe_set_stage_events.argtypes = [P(ctypes.c_void_p), ctypes.c_int32]
     lib.moe_last_error.restype = ctypes.c_char_p
-    for name in ("moe_workspace_init", "moe_route", "moe_layer_forward", "moe_prefill_forward",
+    for name in ("moe_set_stage_events", "moe_workspace_init", "moe_route", "moe_layer_forward", "moe_prefill_forward",
                  "moe_workspace_status"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
@@ -147,6 +148,12 @@ def prefill_forward(x, t: int, router: MoeRouter, plan: MoePrefillPlan, pool: Mo
     _check(lib.moe_prefill_forward(_ptr(x), t, ctypes.byref(router), ctypes.byref(plan),
                                    ctypes.byref(pool), ctypes.byref(shared), _ptr(out),
                                    _stream(stream)))
+
+
+def set_stage_events(events) -> None:
+    """events: list of raw hipEvent_t handles (ints, or None); [] turns the hook off."""
+    arr = (ctypes.c_void_p * max(1, len(events)))(*events)
+    _check(lib.moe_set_stage_events(arr, len(events)))
 
 
 def workspace_status(ws: torch.Tensor, stream=None) -> int:

@@ -1,6 +1,6 @@
 """Build libmoe.so (the HIP library) in-tree with hipcc for gfx950.
 
-    python -m quantized_routed_expert_bf16_amd.build
+    python quantized_routed_expert_bf16_amd/build.py
 
 Every source in csrc/ is compiled to an object file in parallel, then linked
 into quantized_routed_expert_bf16_amd/libmoe.so.  Packed-FP32 instructions are

@@ -63,9 +63,11 @@ WorkspaceLayout workspace_layout(int hidden, int inter, int n_experts, int top_k
     return at;
   };
   const int pf_rows = rows > MOE_MAX_NB ? rows : MOE_MAX_NB;
-  w.counters = take(256 * sizeof(uint32_t));
+  w.counters = take(kSyncWords * sizeof(uint32_t));
   w.act = take(size_t(kSlotStride) * kMaxNb * inter * sizeof(float));
-  w.ypart = take(size_t(kSlotStride) * kMaxNb * hidden * sizeof(float));
+  w.opart = take(size_t(kSlices) * kMaxNb * hidden * sizeof(float));
+  w.slice_logits = take(size_t(kSlices) * kMaxNb * kMaxExperts * sizeof(double) +
+                        size_t(kSlices) * kMaxNb * sizeof(float));
   w.pf_xh = take(size_t(MOE_MAX_PREFILL_ROWS) * hidden * sizeof(_Float16));
   w.pf_act = take(size_t(pf_rows) * (top_k + 1) * inter * sizeof(_Float16));
   w.pf_y = take(size_t(pf_rows) * (top_k + 1) * hidden * sizeof(float));
@@ -114,8 +116,20 @@ static int check_ws(void *ws, size_t ws_bytes, const moe_dims &d, int rows) {
   return MOE_OK;
 }
 
+static thread_local hipEvent_t g_stage_ev[8] = {};
+static thread_local int g_stage_n = 0;
+
 static int launched(hipError_t e, const char *what) {
   if (e != hipSuccess) return fail(MOE_ELAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+// Records the profiling event of stage i (if any) after that stage's launch.
+static int stage_done(int i, hipStream_t s) {
+  if (i < g_stage_n && g_stage_ev[i]) {
+    const hipError_t e = hipEventRecord(g_stage_ev[i], s);
+    if (e != hipSuccess) return fail(MOE_ELAUNCH, "stage event %d: %s", i, hipGetErrorString(e));
+  }
   return MOE_OK;
 }
 
@@ -147,7 +161,7 @@ static RouteArgs route_args(const float *x, int rows, const moe_router *r, const
   a.gamma = gamma;
   a.topk_idx = topk_idx;
   a.topk_w = topk_w;
-  a.counter = static_cast<uint32_t *>(ws) + kCounterRoute;
+  a.counter = static_cast<uint32_t *>(ws) + kSyncRoute;
   return a;
 }
 
@@ -209,33 +223,37 @@ int moe_layer_forward(const float *x, int32_t nb, const moe_router *router, moe_
   if ((rc = check_slots(slots, d, nb))) return rc;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  RouteArgs ra = route_args(x, nb, router, shared, slots->logits, slots->gamma, slots->topk_idx,
-                            slots->topk_w, slots->ws);
-  ra.tab = slots->tab;
-  ra.wmap = slots->wmap;
-  ra.ids = slots->ids;
-  if ((rc = launched(launch_route(ra, s), "route"))) return rc;
-
   const WorkspaceLayout L = workspace_layout(d.hidden, d.inter, d.n_experts, d.top_k, nb);
   uint8_t *ws = static_cast<uint8_t *>(slots->ws);
-  ExpertArgs ea{};
-  ea.pool = pool->base;
-  ea.pool_bytes = pool->bytes;
-  ea.x = x;
-  ea.tab = slots->tab;
-  ea.wmap = slots->wmap;
-  ea.gamma = slots->gamma;
-  ea.shared_rec = shared->rec;
-  ea.hidden = d.hidden;
-  ea.inter = d.inter;
-  ea.act = reinterpret_cast<float *>(ws + L.act);
-  ea.ypart = reinterpret_cast<float *>(ws + L.ypart);
-  ea.tile_count = reinterpret_cast<uint32_t *>(ws + L.counters) + kCounterTiles;
-  ea.status = reinterpret_cast<uint32_t *>(ws + L.counters) + kCounterStatus;
-  ea.out = out;
-  const int max_slots = d.top_k * nb + 1;
-  if ((rc = launched(launch_gate_up(ea, nb, max_slots, s), "gate_up"))) return rc;
-  if ((rc = launched(launch_down(ea, nb, max_slots, s), "down"))) return rc;
+  LayerLaunch l{};
+  l.x = x;
+  l.nb = nb;
+  l.router = router->weight;
+  l.gvec = shared->gate;
+  l.rec = router->rec;
+  l.pool = pool->base;
+  l.pool_bytes = pool->bytes;
+  l.shared_rec = shared->rec;
+  l.hidden = d.hidden;
+  l.inter = d.inter;
+  l.n_experts = d.n_experts;
+  l.top_k = d.top_k;
+  l.logits = slots->logits;
+  l.gamma = slots->gamma;
+  l.topk_idx = slots->topk_idx;
+  l.topk_w = slots->topk_w;
+  l.tab = slots->tab;
+  l.wmap = slots->wmap;
+  l.ids = slots->ids;
+  l.out = out;
+  l.sync = reinterpret_cast<uint32_t *>(ws + L.counters);
+  l.act = reinterpret_cast<float *>(ws + L.act);
+  l.opart = reinterpret_cast<float *>(ws + L.opart);
+  l.slice_logits = reinterpret_cast<double *>(ws + L.slice_logits);
+  l.slice_gamma = reinterpret_cast<float *>(ws + L.slice_logits +
+                                            size_t(kSlices) * kMaxNb * kMaxExperts * sizeof(double));
+  if ((rc = launched(launch_layer(l, s), "layer"))) return rc;
+  if ((rc = stage_done(0, s))) return rc;
   return ok();
 }
 
@@ -267,6 +285,7 @@ int moe_prefill_forward(const float *x, int32_t t, const moe_router *router, moe
   ra.entry_row = plan->entry_row;
   ra.entry_rank = plan->entry_rank;
   if ((rc = launched(launch_prefill_route(ra, s), "prefill route"))) return rc;
+  if ((rc = stage_done(0, s))) return rc;
 
   const WorkspaceLayout L = workspace_layout(d.hidden, d.inter, d.n_experts, d.top_k, t);
   uint8_t *ws = static_cast<uint8_t *>(plan->ws);
@@ -289,16 +308,17 @@ int moe_prefill_forward(const float *x, int32_t t, const moe_router *router, moe
   pa.xh = reinterpret_cast<_Float16 *>(ws + L.pf_xh);
   pa.act = reinterpret_cast<_Float16 *>(ws + L.pf_act);
   pa.y = reinterpret_cast<float *>(ws + L.pf_y);
-  pa.status = reinterpret_cast<uint32_t *>(ws + L.counters) + kCounterStatus;
+  pa.status = reinterpret_cast<uint32_t *>(ws + L.counters) + kSyncStatus;
   pa.out = out;
   if ((rc = launched(launch_prefill_experts(pa, s), "prefill experts"))) return rc;
+  if ((rc = stage_done(1, s))) return rc;
   return ok();
 }
 
 int moe_workspace_status(void *ws, size_t ws_bytes, void *stream) {
-  if (!ws || ws_bytes < 256 * sizeof(uint32_t)) return fail(MOE_EWORKSPACE, "workspace is NULL or too small");
+  if (!ws || ws_bytes < kSyncWords * sizeof(uint32_t)) return fail(MOE_EWORKSPACE, "workspace is NULL or too small");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  uint32_t *word = static_cast<uint32_t *>(ws) + kCounterStatus;
+  uint32_t *word = static_cast<uint32_t *>(ws) + kSyncStatus;
   uint32_t v = 0;
   hipError_t e = hipMemcpyAsync(&v, word, sizeof v, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -308,6 +328,14 @@ int moe_workspace_status(void *ws, size_t ws_bytes, void *stream) {
   if (e != hipSuccess) return fail(MOE_ELAUNCH, "status read failed: %s", hipGetErrorString(e));
   ok();
   return int(v & 0x7fffffff);
+}
+
+int moe_set_stage_events(void *const *events, int32_t n) {
+  if (n < 0 || n > 8) return fail(MOE_EINVAL, "stage events: n %d must be in 0..8", n);
+  if (n > 0 && !events) return fail(MOE_EINVAL, "stage events: events is NULL");
+  for (int i = 0; i < 8; ++i) g_stage_ev[i] = i < n ? static_cast<hipEvent_t>(events[i]) : nullptr;
+  g_stage_n = n;
+  return ok();
 }
 
 const char *moe_last_error(void) { return g_err; }

@@ -1,0 +1,238 @@
+// Device-side helpers of the MoE kernels (gfx950): code unpacking and the
+// per-chunk dot product, bf16 / (scale, bias) decoding, and the cross-block
+// exchange primitives.
+//
+// Cross-block exchange.  Each XCD of the chip has its own L2, so a block on
+// one XCD cannot read another XCD's ordinary stores through its L2.  A
+// device-scope fence would write back and invalidate the whole L2 of every
+// wave that executes it (tens of microseconds per layer when every wave does
+// it), so the kernels never use one.  Instead, data that another block reads
+// in the same launch is stored and loaded with device-coherent (sc1) memory
+// operations, the writer waits for its stores to complete (s_waitcnt) before
+// it bumps a device-coherent atomic counter, and the reader polls that
+// counter before loading.  Data read only by later launches uses ordinary
+// stores (kernel boundaries order them).
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+// ------------------------------------------------------------ decoding
+__device__ inline float byte_f(uint32_t v, int k) { return float((v >> (8 * k)) & 0xffu); }
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ inline float sb_scale(uint32_t w) { return bf16_lo(w); }
+__device__ inline float sb_bias(uint32_t w) { return bf16_hi(w); }
+
+__device__ inline bool record_ok(uint64_t desc, uint64_t pool_bytes, int hidden, int inter) {
+  const int bits = bits_of_tag(desc);
+  if (bits == 0) return false;
+  const uint64_t off = desc & ~uint64_t(255);
+  const RecordLayout L = record_layout(hidden, inter, bits);
+  return off + L.total <= pool_bytes && off + L.total > off;
+}
+
+// Codes of one 32-code chunk of a packed row: 4-bit: w[0..3] (16 B);
+// 2-bit: w[0..1] (8 B); 3-bit: w[0..1] low plane, w[2] high plane (8 + 4 B).
+template <int BITS>
+__device__ inline void load_chunk(const uint8_t *row, int row_codes, int chunk, uint32_t (&w)[4]) {
+  if constexpr (BITS == 4) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(row + chunk * 16);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else if constexpr (BITS == 2) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(row + chunk * 8);
+    w[0] = v.x; w[1] = v.y; w[2] = 0; w[3] = 0;
+  } else {
+    const uint2 v = *reinterpret_cast<const uint2 *>(row + chunk * 8);
+    w[0] = v.x; w[1] = v.y;
+    w[2] = *reinterpret_cast<const uint32_t *>(row + row_codes / 4 + chunk * 4);
+    w[3] = 0;
+  }
+}
+
+// P[b] = sum_t q_t * x(b, t) over one chunk's 32 codes, f32 FMAs.  Codes
+// are expanded with one AND per four codes and a byte->float conversion per
+// code (v_cvt_f32_ubyte); the power-of-two scale of each bit field is undone
+// once per chunk.  `X` supplies the operand four values at a time:
+// X(b, q) returns x(b, 4q .. 4q+3) as a float4, so the caller decides whether
+// they live in registers or in LDS.
+template <int BITS, int NB, typename XSrc>
+__device__ inline void chunk_dot(const uint32_t (&w)[4], const XSrc &X, float (&P)[NB]) {
+  if constexpr (BITS == 4) {
+    // word m holds codes 8m..8m+7: low nibbles = even codes, high = odd (x16)
+    float lo[NB], hi[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) lo[b] = hi[b] = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t l = w[m] & 0x0f0f0f0fu, h = w[m] & 0xf0f0f0f0u;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float4 x0 = X(b, 2 * m), x1 = X(b, 2 * m + 1);
+        lo[b] = fmaf(byte_f(l, 0), x0.x, lo[b]);
+        hi[b] = fmaf(byte_f(h, 0), x0.y, hi[b]);
+        lo[b] = fmaf(byte_f(l, 1), x0.z, lo[b]);
+        hi[b] = fmaf(byte_f(h, 1), x0.w, hi[b]);
+        lo[b] = fmaf(byte_f(l, 2), x1.x, lo[b]);
+        hi[b] = fmaf(byte_f(h, 2), x1.y, hi[b]);
+        lo[b] = fmaf(byte_f(l, 3), x1.z, lo[b]);
+        hi[b] = fmaf(byte_f(h, 3), x1.w, hi[b]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) P[b] = fmaf(hi[b], 0.0625f, lo[b]);
+  } else {
+    // 2-bit field p of byte k of word m holds code 16m+4k+p (x 4^p); 3-bit
+    // adds the high bit from byte k, bit 4m+p, of the high-plane word.
+    float acc[4][NB];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[p][b] = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      float c[4][4];   // [p][k]
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t l = w[m] & (0x03030303u << (2 * p));
+        uint32_t h = 0;
+        if constexpr (BITS == 3) h = w[2] & (0x01010101u << (4 * m + p));
+        // 2^(2+p-4m): scales the high-bit byte value 2^(4m+p) to 4 * 4^p
+        const float hs = (m == 0) ? float(4 << p) : float(4 << p) / 16.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          c[p][k] = byte_f(l, k);
+          if constexpr (BITS == 3) c[p][k] = fmaf(byte_f(h, k), hs, c[p][k]);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float4 xv = X(b, 4 * m + k);     // codes 16m+4k .. 16m+4k+3 (p = 0..3)
+          acc[0][b] = fmaf(c[0][k], xv.x, acc[0][b]);
+          acc[1][b] = fmaf(c[1][k], xv.y, acc[1][b]);
+          acc[2][b] = fmaf(c[2][k], xv.z, acc[2][b]);
+          acc[3][b] = fmaf(c[3][k], xv.w, acc[3][b]);
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      P[b] = acc[0][b] + 0.25f * acc[1][b] + 0.0625f * acc[2][b] + 0.015625f * acc[3][b];
+  }
+}
+
+// Operand sources for chunk_dot.
+template <int NB>
+struct RegX {   // x[b][0..31] in registers
+  const float (&x)[NB][kChunk];
+  __device__ float4 operator()(int b, int q) const {
+    return make_float4(x[b][4 * q], x[b][4 * q + 1], x[b][4 * q + 2], x[b][4 * q + 3]);
+  }
+};
+struct LdsX {   // x(b, t) = p[b * stride + t], 16-byte aligned, in LDS
+  const float *p;
+  int stride;
+  __device__ float4 operator()(int b, int q) const {
+    return *reinterpret_cast<const float4 *>(p + b * stride + 4 * q);
+  }
+};
+
+__device__ inline float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// ------------------------------------------------- wave reductions (DPP)
+// Lane permutations inside 16-lane rows run on the DPP path (a few cycles)
+// instead of the LDS crossbar (ds_bpermute); rows are combined with
+// v_readlane, so the result is uniform across the wave.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i inside each 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i inside each 16
+
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ inline double dpp_d(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_mov_dpp(int(uint32_t(u)), CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp(int(uint32_t(u >> 32)), CTRL, 0xF, 0xF, true);
+  return __longlong_as_double((uint64_t(uint32_t(hi)) << 32) | uint32_t(lo));
+}
+
+// Sum over each group of 8 lanes (all lanes of the group get it).
+__device__ inline float group8_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  return v;
+}
+// Sum over each 16-lane row.
+__device__ inline float row16_sum(float v) {
+  v = group8_sum(v);
+  return v + dpp_f<kDppMirror>(v);
+}
+// Sum over the wave, uniform result.
+__device__ inline float wave_sum(float v) {
+  v = row16_sum(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (a + b) + (c + d);
+}
+__device__ inline double readlane_d(double v, int lane) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane(int(uint32_t(u)), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(int(uint32_t(u >> 32)), lane);
+  return __longlong_as_double((uint64_t(hi) << 32) | lo);
+}
+__device__ inline double wave_sum_d(double v) {
+  v += dpp_d<kDppXor1>(v);
+  v += dpp_d<kDppXor2>(v);
+  v += dpp_d<kDppHalfMirror>(v);
+  v += dpp_d<kDppMirror>(v);
+  return (readlane_d(v, 0) + readlane_d(v, 16)) + (readlane_d(v, 32) + readlane_d(v, 48));
+}
+
+// ------------------------------------------------ cross-block exchange
+template <typename T>
+__device__ inline void st_dev(T *p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ inline T ld_dev(const T *p) {
+  return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 4 consecutive floats (16-byte aligned) with one device-coherent load.
+__device__ inline float4 ld_dev_f4(const float *p) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), (short)0, 16, 0x00020000);
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 16));
+}
+
+// 32 consecutive floats (16-byte aligned) with device-coherent loads.
+__device__ inline void ld_dev_32f(const float *p, float (&v)[kChunk]) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), (short)0, kChunk * 4, 0x00020000);
+#pragma unroll
+  for (int q = 0; q < kChunk / 4; ++q) {
+    const float4 f = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, q * 16, 0, 16));
+    v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+  }
+}
+
+// All of this block's prior stores are complete before thread 0 signals.
+__device__ inline void block_signal(uint32_t *counter, uint32_t inc, uint32_t *prev_out = nullptr) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(counter, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev_out) *prev_out = prev;
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,568 @@
+// The whole decode MoE layer in one persistent launch (gfx950).
+//
+// What it computes is Struct Gpu router_b ("softmax over experts, top-k" over
+// nb rows) followed by experts_b (the routed experts of the union published
+// in the slot table, plus the shared expert, summed per row), with the union
+// and slot table of gpu.rs (union_of: first-seen order; slot_tab entry 62 =
+// resident count, 63 = union size; wmap = per-row weight per slot) built on
+// the device instead of by a host round trip.
+//
+// XCD-aware split.  The grid is 8 slices of blocks (block b belongs to slice
+// b % 8, which the round-robin dispatcher places on XCD b % 8).  Slice x owns
+// columns [x*W, (x+1)*W) of the expert width I (W = I / slices): the gate/up
+// rows of those act values and the matching columns of every down matrix,
+// for every slot of the union.  A slice therefore needs nothing from other
+// slices until the very end:
+//   1. every block stages the nb rows of x in LDS (plus per-32 sums of x);
+//   2. each slice computes the whole router itself (E expert rows + the
+//      shared gate vector as row E, float64 accumulation) -- 512 KB read per
+//      slice, mostly served by the memory-side cache -- and publishes the
+//      logits in its own buffer; meanwhile other blocks of the slice run the
+//      shared expert's gate/up rows, which need no routing;
+//   3. every block of the slice waits for the slice's router blocks, then
+//      ranks the logits and builds the union itself (wave-parallel);
+//   4. gate/up units (slot, 8 row pairs of the slice) write silu(g)*u;
+//      down units (tile of 32 output rows) first load their weights for all
+//      slots, then wait for the slice's gate/up units, and write the slice's
+//      routing-weighted partial rows (sum over slots in slot order, shared
+//      expert last);
+//   5. the slice that completes a row tile last sums the slices' partials in
+//      slice order into `out`;
+//   6. the last block out resets the counters for the next launch.
+// Cross-block data moves through device-coherent loads/stores (see
+// device_common.h), so results do not depend on where blocks actually run;
+// the slice-to-XCD placement only keeps the polling local.  Every wait is
+// bounded: one that runs out sets the abort word and status bit 2, after
+// which every wait falls through, so a launch cannot hang.
+#include "device_common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kTileRowPairs = 8;                      // gate/up unit: 8 row pairs
+constexpr int kPairsPerWave = kTileRowPairs / kWaves;
+constexpr int kRowsPerWave = 8;                       // down unit: 8 rows per wave
+constexpr int kRowsPerTile = kRowsPerWave * kWaves;   // 32 rows per down tile
+constexpr int kSlotBatch = 10;                        // slots per lane per down batch
+constexpr int kStageCols = 256;                       // slot-groups x slice width, per batch
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+struct LayerArgs {
+  LayerLaunch l;
+  int n_slices;      // slices with work (<= 8)
+  int W;             // columns of I per slice
+  int ups;           // gate/up units per slot per slice
+  int tiles;         // down tiles (of kRowsPerTile rows)
+  int per_slice;     // blocks per slice (gridDim.x / 8)
+  int route_blocks;  // router blocks per slice
+};
+
+__device__ inline uint32_t *sw(const LayerArgs &a, int x, int field) {
+  return a.l.sync + kSyncSliceStride * x + field;
+}
+
+__device__ inline void set_status(const LayerArgs &a, uint32_t bits) {
+  __hip_atomic_fetch_or(a.l.sync + kSyncStatus, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Bounded wait until *p >= target (thread 0 polls, then the block proceeds).
+__device__ inline void wait_geq(const LayerArgs &a, const uint32_t *p, uint32_t target) {
+  if (threadIdx.x == 0) {
+    uint32_t it = 0;
+    while (ld_dev(p) < target) {
+      if ((++it & 63) == 0) {
+        if (ld_dev(a.l.sync + kSyncAbort)) break;
+        if (it > kSpinLimit) {
+          st_dev(a.l.sync + kSyncAbort, 1u);
+          set_status(a, 4u);
+          break;
+        }
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+}
+
+template <int NB>
+struct Shared {
+  int sel[NB][kMaxTopK];
+  double selv[NB][kMaxTopK];
+  float wsel[NB][kMaxTopK];
+  int uid[kSlotStride];
+  float wslot[NB][kSlotStride];   // routing weight per slot (index u: gamma)
+  uint64_t desc[kSlotStride];     // descriptor per slot (index u: shared expert)
+  float gam[NB];
+  int u;
+  uint32_t prev;
+};
+
+// ----------------------------------------------------------------- route
+template <int NB>
+__device__ void router_rows(const LayerArgs &a, const float *xs, int lr, double *lg, float *gm) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int H = a.l.hidden, E = a.l.n_experts;
+  for (int e = lr * kWaves + wave; e <= E; e += a.per_slice * kWaves) {
+    const uint16_t *w = e < E ? a.l.router + size_t(e) * H : a.l.gvec;
+    double acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = 0.0;
+    for (int i0 = lane * 8; i0 < H; i0 += 512) {
+      const uint4 wv = *reinterpret_cast<const uint4 *>(w + i0);
+      const float wf[8] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y),
+                           bf16_lo(wv.z), bf16_hi(wv.z), bf16_lo(wv.w), bf16_hi(wv.w)};
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float4 x0 = *reinterpret_cast<const float4 *>(xs + b * H + i0);
+        const float4 x1 = *reinterpret_cast<const float4 *>(xs + b * H + i0 + 4);
+        const float xf[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[b] = fma(double(wf[t]), double(xf[t]), acc[b]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const double v = wave_sum_d(acc[b]);
+      if (lane == 0) {
+        if (e < E)
+          st_dev(lg + b * kMaxExperts + e, v);
+        else
+          st_dev(gm + b, float(1.0 / (1.0 + exp(-v))));
+      }
+    }
+  }
+}
+
+// Top-k, weights and union of the slice's published logits (every block).
+// The rank of expert e in row b is the number of experts ordered before it
+// by (logit descending, id ascending); every thread ranks its experts against
+// the whole row, read two logits at a time as LDS broadcasts.  Lanes < k of
+// wave b take one exp each for the softmax; the union is one ballot.
+template <int NB>
+__device__ void build_routing(const LayerArgs &a, Shared<NB> &s, const double *lg, const float *gm,
+                              const uint64_t *rec_lds, double *lgs) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int E = a.l.n_experts, k = a.l.top_k;
+  const int Ep = (E + 7) & ~7;    // rows padded to a multiple of 8 with -inf
+  for (int p = threadIdx.x; p < NB * Ep; p += kThreads) {
+    const int b = p / Ep, e = p - b * Ep;
+    lgs[b * Ep + e] = e < E ? ld_dev(lg + b * kMaxExperts + e) : -__builtin_inf();
+  }
+  if (threadIdx.x < NB) s.gam[threadIdx.x] = ld_dev(gm + threadIdx.x);
+  for (int p = threadIdx.x; p < NB * kMaxTopK; p += kThreads) s.sel[p / kMaxTopK][p % kMaxTopK] = 0;
+  __syncthreads();
+  for (int p = threadIdx.x; p < NB * E; p += kThreads) {
+    const int b = p / E, e = p - b * E;
+    const double v = lgs[b * Ep + e];
+    const double2 *row = reinterpret_cast<const double2 *>(lgs + b * Ep);
+    int rank = 0;
+    // branch-free: four broadcast reads in flight per step
+    for (int f2 = 0; f2 < Ep / 2; f2 += 4) {
+      const double2 o0 = row[f2], o1 = row[f2 + 1], o2 = row[f2 + 2], o3 = row[f2 + 3];
+      const int f = 2 * f2;
+      rank += int(o0.x > v) + int(o0.y > v) + int(o1.x > v) + int(o1.y > v) +
+              int(o2.x > v) + int(o2.y > v) + int(o3.x > v) + int(o3.y > v);
+      rank += (int(o0.x == v) & int(f < e)) + (int(o0.y == v) & int(f + 1 < e)) +
+              (int(o1.x == v) & int(f + 2 < e)) + (int(o1.y == v) & int(f + 3 < e)) +
+              (int(o2.x == v) & int(f + 4 < e)) + (int(o2.y == v) & int(f + 5 < e)) +
+              (int(o3.x == v) & int(f + 6 < e)) + (int(o3.y == v) & int(f + 7 < e));
+    }
+    if (rank < k) {
+      s.sel[b][rank] = e;
+      s.selv[b][rank] = v;
+    }
+  }
+  __syncthreads();
+  if (wave < NB) {
+    const int b = wave;
+    double ex = 0.0;
+    if (lane < k) ex = exp(s.selv[b][lane] - s.selv[b][0]);
+    const double sum = wave_sum_d(ex);
+    if (lane < k) s.wsel[b][lane] = float(ex / sum);
+  }
+  if (wave == 0) {
+    // first-seen union over the row-major (row, rank) list
+    const int n = NB * k;
+    int e = -1, first = 0;
+    if (lane < n) {
+      e = s.sel[lane / k][lane % k];
+      first = 1;
+      for (int q = 0; q < lane; ++q) first &= (s.sel[q / k][q % k] != e);
+    }
+    const uint64_t mask = __ballot(first);
+    const int slot = __popcll(mask & ((uint64_t(1) << lane) - 1));
+    if (first) s.uid[slot] = e;
+    if (lane == 0) s.u = __popcll(mask);
+  }
+  __syncthreads();
+  const int u = s.u;
+  for (int j = threadIdx.x; j < kSlotStride; j += kThreads) {
+    s.desc[j] = j < u ? rec_lds[s.uid[j]] : (j == u ? a.l.shared_rec : 0);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      float w = 0.0f;
+      if (j < u) {
+        for (int r = 0; r < k; ++r)
+          if (s.sel[b][r] == s.uid[j]) w = s.wsel[b][r];
+      } else if (j == u) {
+        w = s.gam[b];
+      }
+      s.wslot[b][j] = w;
+    }
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {   // caller-visible routing tables
+    for (int j = threadIdx.x; j < kSlotStride; j += kThreads) {
+      a.l.ids[j] = j < u ? uint32_t(s.uid[j]) : 0u;
+      a.l.tab[j] = (j == MOE_RESIDENT_ENTRY || j == MOE_UNION_ENTRY) ? uint64_t(u)
+                                                                    : (j < u ? s.desc[j] : 0);
+      for (int b = 0; b < kMaxNb; ++b)
+        a.l.wmap[b * kSlotStride + j] = (b < NB && j < u) ? s.wslot[b < NB ? b : 0][j] : 0.0f;
+    }
+    for (int p = threadIdx.x; p < NB * k; p += kThreads) {
+      a.l.topk_idx[p] = uint32_t(s.sel[p / k][p % k]);
+      a.l.topk_w[p] = s.wsel[p / k][p % k];
+    }
+    for (int p = threadIdx.x; p < NB * E; p += kThreads) a.l.logits[p] = lgs[(p / E) * Ep + p % E];
+    if (threadIdx.x < NB) a.l.gamma[threadIdx.x] = s.gam[threadIdx.x];
+  }
+}
+
+// ------------------------------------------------------------ gate / up
+// 8 row pairs (gate j, up j) of one slot; each wave takes 2, a lane one
+// 32-code chunk of the H inputs (CPL chunks when H > 2048).
+template <int NB, int CPL, int BITS>
+__device__ void gate_up_unit(const LayerArgs &a, const uint8_t *rec, int j0, int act_slot,
+                             const float *xs, const float *xsum) {
+  const int lane = threadIdx.x & 63;
+  const int H = a.l.hidden, I = a.l.inter;
+  const RecordLayout L = record_layout(H, I, BITS);
+  const int n_chunks = H / kChunk, gpr = H / kGroup;
+  const uint8_t *codes = rec + L.gu_codes;
+  const uint32_t *sb = reinterpret_cast<const uint32_t *>(rec + L.gu_sb);
+
+  uint32_t w[kPairsPerWave][2][CPL][4];
+  uint32_t s[kPairsPerWave][2][CPL];
+#pragma unroll
+  for (int p = 0; p < kPairsPerWave; ++p)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 2 * (j0 + p) + h;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int chunk = lane + 64 * c;
+        if (chunk < n_chunks) {
+          load_chunk<BITS>(codes + size_t(row) * L.gu_row_bytes, H, chunk, w[p][h][c]);
+          s[p][h][c] = sb[size_t(row) * gpr + chunk / 2];
+        } else {
+          w[p][h][c][0] = w[p][h][c][1] = w[p][h][c][2] = w[p][h][c][3] = 0;
+          s[p][h][c] = 0;
+        }
+      }
+    }
+  float v[kPairsPerWave][2][NB];
+#pragma unroll
+  for (int p = 0; p < kPairsPerWave; ++p)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) v[p][h][b] = 0.0f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int chunk = lane + 64 * c;
+    const bool live = chunk < n_chunks;
+    float xr[NB][kChunk];
+    float xsm[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int q = 0; q < kChunk / 4; ++q) {
+        float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (live) f = *reinterpret_cast<const float4 *>(xs + b * H + chunk * kChunk + 4 * q);
+        xr[b][4 * q] = f.x; xr[b][4 * q + 1] = f.y; xr[b][4 * q + 2] = f.z; xr[b][4 * q + 3] = f.w;
+      }
+      xsm[b] = live ? xsum[b * (H / kChunk) + chunk] : 0.0f;
+    }
+#pragma unroll
+    for (int p = 0; p < kPairsPerWave; ++p)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float P[NB];
+        chunk_dot<BITS, NB>(w[p][h][c], RegX<NB>{xr}, P);
+        const float sc = sb_scale(s[p][h][c]), bi = sb_bias(s[p][h][c]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) v[p][h][b] += fmaf(sc, P[b], bi * xsm[b]);
+      }
+  }
+#pragma unroll
+  for (int p = 0; p < kPairsPerWave; ++p) {
+    float g = 0.0f, u = 0.0f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float gs = wave_sum(v[p][0][b]), us = wave_sum(v[p][1][b]);
+      if (lane == b) { g = gs; u = us; }
+    }
+    if (lane < NB) st_dev(a.l.act + (size_t(act_slot) * kMaxNb + lane) * I + j0 + p, silu_mul(g, u));
+  }
+}
+
+template <int NB, int CPL>
+__device__ void run_gate_up(const LayerArgs &a, int x, uint64_t desc, int act_slot, int unit,
+                            const float *xs, const float *xsum) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j0 = x * a.W + unit * kTileRowPairs + wave * kPairsPerWave;
+  if (record_ok(desc, a.l.pool_bytes, a.l.hidden, a.l.inter)) {
+    const uint8_t *rec = a.l.pool + (desc & ~uint64_t(255));
+    switch (bits_of_tag(desc)) {
+      case 4: gate_up_unit<NB, CPL, 4>(a, rec, j0, act_slot, xs, xsum); break;
+      case 3: gate_up_unit<NB, CPL, 3>(a, rec, j0, act_slot, xs, xsum); break;
+      default: gate_up_unit<NB, CPL, 2>(a, rec, j0, act_slot, xs, xsum); break;
+    }
+  } else {
+    if (threadIdx.x == 0) set_status(a, 1u);
+    if (lane < NB * kPairsPerWave)
+      st_dev(a.l.act + (size_t(act_slot) * kMaxNb + lane / kPairsPerWave) * a.l.inter + j0 +
+                 lane % kPairsPerWave, 0.0f);
+  }
+  block_signal(sw(a, x, kSliceGu), 1u);
+}
+
+// ----------------------------------------------------------------- down
+// A down tile: 32 output rows of the slice's columns, every slot.  Lane
+// (row rw, chunk c, slot group g) of a wave handles row rw, 32-code chunk c
+// of the slice, and slots g, g + SG, ...; weights for the lane's slots are
+// loaded before the wait for the slice's gate/up units.
+template <int NB>
+__device__ void run_down(const LayerArgs &a, Shared<NB> &sh, int x, int tile, float *act_lds,
+                         float *asum_lds) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int H = a.l.hidden, I = a.l.inter, W = a.W;
+  const int cpr = W / kChunk;                 // chunks per row in the slice (1..8)
+  const int sg = 8 / cpr;                     // slot groups per row
+  const int idx = lane & 7;
+  const int rw = lane >> 3, c = idx % cpr, g = idx / cpr;
+  const int row = tile * kRowsPerTile + wave * kRowsPerWave + rw;
+  const int col = x * W + c * kChunk;        // first column of this lane's chunk
+  const int grp = col / kGroup, half = (col % kGroup) / kChunk;
+  const int u = sh.u, n_slots = u + 1;
+  float acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = 0.0f;
+
+  for (int s0 = 0; s0 < n_slots; s0 += sg * kSlotBatch) {
+    // 1. this lane's weights for the batch
+    uint32_t w[kSlotBatch][4];
+    uint32_t sbw[kSlotBatch];
+    int bits[kSlotBatch];
+#pragma unroll
+    for (int m = 0; m < kSlotBatch; ++m) {
+      const int slot = s0 + g + sg * m;
+      bits[m] = 0;
+      w[m][0] = w[m][1] = w[m][2] = w[m][3] = 0;
+      sbw[m] = 0;
+      if (slot < n_slots) {
+        const uint64_t desc = sh.desc[slot];
+        if (record_ok(desc, a.l.pool_bytes, H, I)) {
+          const int bt = bits_of_tag(desc);
+          const RecordLayout L = record_layout(H, I, bt);
+          const uint8_t *rec = a.l.pool + (desc & ~uint64_t(255));
+          const uint8_t *grow = rec + L.d_codes + (size_t(grp) * H + row) * (kGroup * bt / 8);
+          if (bt == 4) load_chunk<4>(grow, kGroup, half, w[m]);
+          else if (bt == 3) load_chunk<3>(grow, kGroup, half, w[m]);
+          else load_chunk<2>(grow, kGroup, half, w[m]);
+          sbw[m] = reinterpret_cast<const uint32_t *>(rec + L.d_sb)[size_t(grp) * H + row];
+          bits[m] = bt;
+        } else if (rw == 0 && c == 0) {
+          set_status(a, 1u);
+        }
+      }
+    }
+    // 2. the slice's act values must be complete
+    if (s0 == 0) wait_geq(a, sw(a, x, kSliceGu), uint32_t(n_slots * a.ups));
+    // 3. stage the batch's act (slice columns) and per-chunk sums in LDS
+    const int nb_slots = min(n_slots - s0, sg * kSlotBatch);
+    __syncthreads();
+    for (int i = threadIdx.x; i < nb_slots * NB * (W / 4); i += kThreads) {
+      const int q = i % (W / 4), b = (i / (W / 4)) % NB, sl = i / (W / 4) / NB;
+      const int slot = s0 + sl;
+      const int ps = slot < u ? slot : kSharedSlot;
+      const float *src = a.l.act + (size_t(ps) * kMaxNb + b) * I + x * W + 4 * q;
+      *reinterpret_cast<float4 *>(act_lds + (sl * NB + b) * W + 4 * q) = ld_dev_f4(src);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nb_slots * NB * cpr; i += kThreads) {
+      const float *p = act_lds + (i / cpr) * W + (i % cpr) * kChunk;
+      float sm = 0.0f;
+#pragma unroll
+      for (int t = 0; t < kChunk; ++t) sm += p[(t + i) & (kChunk - 1)];   // no bank conflicts
+      asum_lds[i] = sm;
+    }
+    __syncthreads();
+    // 4. accumulate the lane's slots
+#pragma unroll
+    for (int m = 0; m < kSlotBatch; ++m) {
+      if (bits[m] == 0) continue;
+      const int sl = g + sg * m;
+      const int slot = s0 + sl;
+      float P[NB];
+      const LdsX ax{act_lds + sl * NB * W + c * kChunk, W};
+      if (bits[m] == 4) chunk_dot<4, NB>(w[m], ax, P);
+      else if (bits[m] == 3) chunk_dot<3, NB>(w[m], ax, P);
+      else chunk_dot<2, NB>(w[m], ax, P);
+      const float sc = sb_scale(sbw[m]), bi = sb_bias(sbw[m]);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        acc[b] = fmaf(sh.wslot[b][slot], fmaf(sc, P[b], bi * asum_lds[(sl * NB + b) * cpr + c]), acc[b]);
+    }
+  }
+  // sum the row's 8 lanes (chunks x slot groups) and publish the slice partial
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = group8_sum(acc[b]);
+  if (idx == 0)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) st_dev(a.l.opart + (size_t(x) * kMaxNb + b) * H + row, acc[b]);
+
+  block_signal(a.l.sync + kSyncTile + tile, 1u, &sh.prev);
+  __syncthreads();
+  if (sh.prev == uint32_t(a.n_slices - 1)) {   // last slice of this tile: combine
+    for (int i = threadIdx.x; i < kRowsPerTile * NB; i += kThreads) {
+      const int b = i / kRowsPerTile, r = tile * kRowsPerTile + i % kRowsPerTile;
+      float v = 0.0f;
+      for (int q = 0; q < a.n_slices; ++q) v += ld_dev(a.l.opart + (size_t(q) * kMaxNb + b) * H + r);
+      a.l.out[size_t(b) * H + r] = v;
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- kernel
+template <int NB, int CPL>
+__global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
+  extern __shared__ float4 dyn[];
+  __shared__ Shared<NB> sh;
+  __shared__ uint64_t rec_lds[kMaxExperts];
+  const int H = a.l.hidden;
+  float *xs = reinterpret_cast<float *>(dyn);           // [NB][H]
+  float *xsum = xs + NB * H;                            // [NB][H/32]
+  float *act_lds = xsum + NB * (H / kChunk);            // [batch slots][NB][W]; logits first
+  static_assert(kStageCols * kSlotBatch >= 2 * kMaxExperts, "logits scratch must fit");
+  float *asum_lds = act_lds + kStageCols * kSlotBatch * NB;
+
+  const int x = blockIdx.x % kSlices, lr = blockIdx.x / kSlices;
+  const int P = a.per_slice;
+
+  if (x < a.n_slices) {
+    for (int e = threadIdx.x; e < a.l.n_experts; e += kThreads) rec_lds[e] = a.l.rec[e];
+    for (int i = threadIdx.x * 4; i < NB * H; i += kThreads * 4)
+      *reinterpret_cast<float4 *>(xs + i) = *reinterpret_cast<const float4 *>(a.l.x + i);
+    __syncthreads();
+    for (int i = threadIdx.x; i < NB * (H / kChunk); i += kThreads) {
+      const float *p = xs + i * kChunk;
+      float sm = 0.0f;
+#pragma unroll
+      for (int t = 0; t < kChunk; ++t) sm += p[(t + i) & (kChunk - 1)];   // no bank conflicts
+      xsum[i] = sm;
+    }
+    __syncthreads();
+
+    double *lg = a.l.slice_logits + size_t(x) * kMaxNb * kMaxExperts;
+    float *gm = a.l.slice_gamma + x * kMaxNb;
+    if (lr < a.route_blocks) {
+      router_rows<NB>(a, xs, lr, lg, gm);
+      block_signal(sw(a, x, kSliceRoute), 1u);
+    }
+    // the shared expert's gate/up units need no routing
+    for (int i = ((lr - a.route_blocks) % P + P) % P; i < a.ups; i += P)
+      run_gate_up<NB, CPL>(a, x, a.l.shared_rec, kSharedSlot, i, xs, xsum);
+
+    wait_geq(a, sw(a, x, kSliceRoute), uint32_t(a.route_blocks));
+    // the logits scratch lives in the (not yet used) act staging area
+    build_routing<NB>(a, sh, lg, gm, rec_lds, reinterpret_cast<double *>(act_lds));
+    const int u = sh.u;
+    const int n_gu = u * a.ups;
+    const int n_total = n_gu + a.tiles;
+    for (int i = ((lr - a.route_blocks - a.ups) % P + P) % P; i < n_total; i += P) {
+      if (i < n_gu) {
+        const int slot = i / a.ups;
+        run_gate_up<NB, CPL>(a, x, sh.desc[slot], slot, i - slot * a.ups, xs, xsum);
+      } else {
+        run_down<NB>(a, sh, x, i - n_gu, act_lds, asum_lds);
+      }
+    }
+  }
+
+  // two-level exit count; the last block out resets the counters
+  block_signal(sw(a, x, kSliceExit), 1u, &sh.prev);
+  __syncthreads();
+  if (sh.prev == uint32_t(P - 1)) {
+    block_signal(a.l.sync + kSyncExit, 1u, &sh.prev);
+    __syncthreads();
+    if (sh.prev == uint32_t(kSlices - 1)) {
+      for (int i = threadIdx.x; i < kSyncWords; i += kThreads)
+        if (i != kSyncStatus) st_dev(a.l.sync + i, 0u);
+    }
+  }
+}
+
+size_t dyn_lds_bytes(int nb, int hidden) {
+  // x, per-32 sums of x, one batch of staged act values, their per-chunk sums
+  return sizeof(float) * (size_t(nb) * hidden + size_t(nb) * (hidden / kChunk) +
+                          size_t(kStageCols) * kSlotBatch * nb + size_t(8) * kSlotBatch * nb);
+}
+
+struct LaunchCache {
+  int device = -1;
+  int blocks_per_cu[kMaxNb + 1][3] = {};
+  int cus = 0;
+};
+thread_local LaunchCache g_cache;
+
+template <int NB, int CPL>
+hipError_t launch_nb(LayerArgs &a, hipStream_t s) {
+  const size_t lds = dyn_lds_bytes(NB, a.l.hidden);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (g_cache.device != dev) {
+    g_cache = LaunchCache();
+    g_cache.device = dev;
+    e = hipDeviceGetAttribute(&g_cache.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+  }
+  int &per_cu = g_cache.blocks_per_cu[NB][CPL];
+  if (per_cu == 0) {
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, layer_kernel<NB, CPL>, kThreads,
+                                                     dyn_lds_bytes(NB, CPL * 64 * kChunk));
+    if (e != hipSuccess) return e;
+    if (per_cu < 1) return hipErrorInvalidConfiguration;
+    if (per_cu > 2) per_cu = 2;
+  }
+  const int grid = (per_cu * g_cache.cus) / kSlices * kSlices;
+  a.per_slice = grid / kSlices;
+  a.route_blocks = min(a.per_slice, (a.l.n_experts + 1 + kWaves - 1) / kWaves);
+  hipLaunchKernelGGL((layer_kernel<NB, CPL>), dim3(grid), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_layer(const LayerLaunch &l, hipStream_t s) {
+  LayerArgs a{};
+  a.l = l;
+  a.n_slices = min(kSlices, l.inter / kChunk);
+  a.W = l.inter / a.n_slices;
+  a.ups = a.W / kTileRowPairs;
+  a.tiles = l.hidden / kRowsPerTile;
+  if (a.tiles > kMaxDownTiles || a.W / kChunk > 8 || a.W % kTileRowPairs) return hipErrorInvalidValue;
+  const bool two = l.hidden > 64 * kChunk;
+  switch (l.nb) {
+    case 1: return two ? launch_nb<1, 2>(a, s) : launch_nb<1, 1>(a, s);
+    case 2: return two ? launch_nb<2, 2>(a, s) : launch_nb<2, 1>(a, s);
+    case 3: return two ? launch_nb<3, 2>(a, s) : launch_nb<3, 1>(a, s);
+    default: return two ? launch_nb<4, 2>(a, s) : launch_nb<4, 1>(a, s);
+  }
+}
+
+}  // namespace moe

@@ -66,27 +66,38 @@ struct RouteArgs {
   uint32_t *counter;       // one zero-initialised word, reset by the last block
 };
 
-struct ExpertArgs {
+// One decode layer launch (the fused persistent kernel of layer.hip).
+struct LayerLaunch {
+  const float *x;            // [nb][H]
+  int nb;
+  const uint16_t *router;    // [E][H] bf16
+  const uint16_t *gvec;      // [H] bf16
+  const uint64_t *rec;       // [E]
   const uint8_t *pool;
   uint64_t pool_bytes;
-  const float *x;          // [nb][H]
-  const uint64_t *tab;     // [64] slot table written by the route kernel
-  const float *wmap;       // [4][64]
-  const float *gamma;      // [nb]
   uint64_t shared_rec;
-  int hidden, inter;
-  float *act;              // [64][4][I]  silu(g)*u per slot and row
-  float *ypart;            // [64][4][H]  weighted down output per slot and row
-  uint32_t *tile_count;    // [H / rows-per-tile] zero-initialised counters
-  uint32_t *status;        // bit 0: a descriptor was out of range
-  float *out;              // [nb][H]
+  int hidden, inter, n_experts, top_k;
+  double *logits;            // [nb][E]
+  float *gamma;              // [nb]
+  uint32_t *topk_idx;        // [nb][k]
+  float *topk_w;             // [nb][k]
+  uint64_t *tab;             // [64]
+  float *wmap;               // [4][64]
+  uint32_t *ids;             // [64]
+  float *out;                // [nb][H]
+  uint32_t *sync;            // 256 counter words (workspace head)
+  float *act;                // [64][4][I]
+  float *opart;              // [8][4][H]  per-slice partial outputs
+  double *slice_logits;      // [8][4][256] per-slice router logits
+  float *slice_gamma;        // [8][4]
 };
 
 // Workspace layout (decode and prefill share the head).
 struct WorkspaceLayout {
-  size_t counters;     // 256 u32 counter / status words
+  size_t counters;     // kSyncWords u32 counter / status words
   size_t act;          // decode: [64][4][I] f32
-  size_t ypart;        // decode: [64][4][H] f32
+  size_t opart;        // decode: [8][4][H] f32 per-slice partial outputs
+  size_t slice_logits; // decode: [8][4][256] f64, [8][4] f32 gamma after it
   size_t pf_xh;        // prefill: [32][H] f16 activations
   size_t pf_act;       // prefill: [t*k + t][I] f16 activations per CSR entry
   size_t pf_y;         // prefill: [t][k+1][H] f32 weighted outputs per (row, rank)
@@ -95,17 +106,26 @@ struct WorkspaceLayout {
 
 WorkspaceLayout workspace_layout(int hidden, int inter, int n_experts, int top_k, int rows);
 
-// word indices inside the counter block
-constexpr int kCounterRoute = 0;
-constexpr int kCounterStatus = 1;
-constexpr int kCounterTiles = 64;   // 64..255: per-tile counters of the down kernel
-constexpr int kMaxTiles = 192;
+// Counter block at the workspace head: kSyncWords u32 words.  Words that
+// many blocks poll sit on their own 128-byte lines.
+constexpr int kSyncWords = 1024;
+constexpr int kSlices = 8;                  // logical XCDs of the decode kernel
+constexpr int kSyncSliceStride = 64;        // slice x owns words [64x, 64x + 64)
+constexpr int kSliceRoute = 0;              //   router blocks of the slice arrived
+constexpr int kSliceGu = 32;                //   gate/up units of the slice done
+constexpr int kSliceExit = 48;              //   blocks of the slice that left
+constexpr int kSyncRoute = 512;             // standalone route kernel: blocks arrived
+constexpr int kSyncStatus = 520;            // bit 0: bad descriptor skipped; bit 2: a wait ran out
+constexpr int kSyncExit = 528;              // slices whose blocks all left
+constexpr int kSyncAbort = 576;             // set when a wait ran out: all waits fall through
+constexpr int kSyncTile = 640;              // 256 words: slices done per down row tile
+constexpr int kMaxDownTiles = 256;
 
 // ------------------------------------------------------------- launchers
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
 hipError_t launch_prefill_route(const RouteArgs &a, hipStream_t s);
-hipError_t launch_gate_up(const ExpertArgs &a, int nb, int max_slots, hipStream_t s);
-hipError_t launch_down(const ExpertArgs &a, int nb, int max_slots, hipStream_t s);
+hipError_t launch_layer(const LayerLaunch &l, hipStream_t s);
+int decode_rows_per_tile(int inter);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 
 struct PrefillArgs {

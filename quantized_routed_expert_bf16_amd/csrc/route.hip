@@ -12,22 +12,13 @@
 // of exact bf16 x f32 products, then the last block to finish (a device-scope
 // counter) ranks the logits and publishes the routing tables.  No host round
 // trip and no second launch.
-#include "moe_internal.h"
+#include "device_common.h"
 
 namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-
-__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ inline double wave_sum_f64(double v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
 
 // Logits of rows [row0, row0+NV) for router row `e` (e == E: shared gate).
 template <int NV>
@@ -51,12 +42,12 @@ __device__ inline void router_rows(const RouteArgs &a, int e, int row0, int lane
   }
 #pragma unroll
   for (int b = 0; b < NV; ++b) {
-    const double s = wave_sum_f64(acc[b]);
+    const double s = wave_sum_d(acc[b]);
     if (lane == 0) {
       if (e < a.n_experts)
-        a.logits[size_t(row0 + b) * a.n_experts + e] = s;
+        st_dev(a.logits + size_t(row0 + b) * a.n_experts + e, s);
       else
-        a.gamma[row0 + b] = float(1.0 / (1.0 + exp(-s)));
+        st_dev(a.gamma + row0 + b, float(1.0 / (1.0 + exp(-s))));
     }
   }
 }
@@ -77,21 +68,13 @@ __device__ inline void router_matvec(const RouteArgs &a) {
   }
 }
 
-// Returns true in the one block that arrives last; all its threads then see
-// every other block's logits.
+// Returns true in the one block that arrives last; it then reads the other
+// blocks' logits with device-coherent loads.
 __device__ inline bool arrive_last(uint32_t *counter) {
-  __shared__ int last;
-  __threadfence();
+  __shared__ uint32_t prev;
+  block_signal(counter, 1u, &prev);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev =
-        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    last = (prev == gridDim.x - 1);
-  }
-  __syncthreads();
-  if (!last) return false;
-  __threadfence();
-  return true;
+  return prev == gridDim.x - 1;
 }
 
 // Top-k of `rows` rows from logits in LDS: rank of expert e in row b is the
@@ -141,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void route_decode_kernel(RouteArgs a) {
   __shared__ int first[kMaxNb * kMaxTopK];
   __shared__ int uid[kSlotStride];
   const int E = a.n_experts, k = a.top_k, nb = a.rows;
-  for (int p = threadIdx.x; p < nb * E; p += kThreads) lg[p] = a.logits[p];
+  for (int p = threadIdx.x; p < nb * E; p += kThreads) lg[p] = ld_dev(a.logits + p);
   __syncthreads();
   rank_topk(lg, nb, E, k, sel);
   __syncthreads();
@@ -182,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void route_decode_kernel(RouteArgs a) {
       a.wmap[b * kSlotStride + j] = w;
     }
   }
-  if (threadIdx.x == 0) __hip_atomic_store(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) st_dev(a.counter, 0u);
 }
 
 __global__ __launch_bounds__(kThreads) void route_prefill_kernel(RouteArgs a) {
@@ -195,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void route_prefill_kernel(RouteArgs a) {
   __shared__ float wsel[kRows * kMaxTopK];
   __shared__ int cnt[kMaxExperts + 1];
   const int E = a.n_experts, k = a.top_k, t = a.rows;
-  for (int p = threadIdx.x; p < t * E; p += kThreads) lg[p] = a.logits[p];
+  for (int p = threadIdx.x; p < t * E; p += kThreads) lg[p] = ld_dev(a.logits + p);
   __syncthreads();
   rank_topk(lg, t, E, k, sel);
   __syncthreads();
@@ -229,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void route_prefill_kernel(RouteArgs a) {
           ++pos;
         }
   }
-  if (threadIdx.x == 0) __hip_atomic_store(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) st_dev(a.counter, 0u);
 }
 
 __global__ void fill_zero_kernel(uint4 *p, size_t n16) {

@@ -8,13 +8,15 @@ take their inputs from here, so the two sides always see the same bits.
 Record layout written here (one routed or shared expert = one record in a
 byte pool; every section starts on a 256-byte boundary):
 
-  section   rows            bytes per row          content
-  GU codes  2*I (gate j at  H*bits/8               packed codes, input dim H
-            row 2j, up j
-            at row 2j+1)
-  GU sb     2*I             (H/64)*4               (scale, bias) bf16 pairs
-  D codes   H               I*bits/8               packed codes, input dim I
-  D sb      H               (I/64)*4               (scale, bias) bf16 pairs
+  section   layout                                 content
+  GU codes  2*I rows x H*bits/8 bytes (gate j at   packed codes, input dim H
+            row 2j, up j at row 2j+1)
+  GU sb     2*I rows x (H/64) words                (scale, bias) bf16 pairs
+  D codes   I/64 column groups, each H rows x      packed codes, input dim I,
+            64*bits/8 bytes (group g of row r =    group-major
+            codes 64g..64g+63 of row r packed as
+            a 64-code row)
+  D sb      I/64 column groups, each H words       (scale, bias) bf16 pairs
 
 Code packing inside a row (little-endian u32 words):
   4-bit: code i is bits [4*(i%8), 4*(i%8)+4) of word i//8.
@@ -135,8 +137,12 @@ def write_record(pool: np.ndarray, offset: int, hidden: int, inter: int, bits: i
 
     put("gu_codes", pack_codes(gu_codes, bits))
     put("gu_sb", sb_words(gu_s, gu_b))
-    put("d_codes", pack_codes(d_codes, bits))
-    put("d_sb", sb_words(d_s, d_b))
+    d_codes = np.asarray(d_codes)
+    n_groups = d_codes.shape[1] // GROUP
+    # group-major: [group][row][64 codes packed]
+    grouped = d_codes.reshape(d_codes.shape[0], n_groups, GROUP).transpose(1, 0, 2)
+    put("d_codes", pack_codes(grouped.reshape(-1, GROUP), bits))
+    put("d_sb", np.ascontiguousarray(sb_words(d_s, d_b).T))
     return offset | TAG_OF_BITS[bits]
 
 
