@@ -68,9 +68,11 @@ WorkspaceLayout workspace_layout(int hidden, int inter, int n_experts, int top_k
   w.opart = take(size_t(kSlices) * kMaxNb * hidden * sizeof(float));
   w.slice_logits = take(size_t(kSlices) * kMaxNb * kMaxExperts * sizeof(double) +
                         size_t(kSlices) * kMaxNb * sizeof(float));
-  w.pf_xh = take(size_t(MOE_MAX_PREFILL_ROWS) * hidden * sizeof(_Float16));
-  w.pf_act = take(size_t(pf_rows) * (top_k + 1) * inter * sizeof(_Float16));
+  w.pf_xh = take(size_t(2) * MOE_MAX_PREFILL_ROWS * hidden * sizeof(_Float16));
+  w.pf_xg = take(size_t(MOE_MAX_PREFILL_ROWS) * (hidden / kGroup) * sizeof(float));
+  w.pf_act = take(size_t(pf_rows) * (top_k + 1) * inter * sizeof(float));
   w.pf_y = take(size_t(pf_rows) * (top_k + 1) * hidden * sizeof(float));
+  w.pf_meta = take(size_t(1 + kMaxExperts) * sizeof(int32_t));
   w.total = pos;
   return w;
 }
@@ -279,14 +281,6 @@ int moe_prefill_forward(const float *x, int32_t t, const moe_router *router, moe
   if ((rc = check_ws(plan->ws, plan->ws_bytes, d, t))) return rc;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  RouteArgs ra = route_args(x, t, router, shared, plan->logits, plan->gamma, plan->topk_idx,
-                            plan->topk_w, plan->ws);
-  ra.expert_ptr = plan->expert_ptr;
-  ra.entry_row = plan->entry_row;
-  ra.entry_rank = plan->entry_rank;
-  if ((rc = launched(launch_prefill_route(ra, s), "prefill route"))) return rc;
-  if ((rc = stage_done(0, s))) return rc;
-
   const WorkspaceLayout L = workspace_layout(d.hidden, d.inter, d.n_experts, d.top_k, t);
   uint8_t *ws = static_cast<uint8_t *>(plan->ws);
   PrefillArgs pa{};
@@ -306,13 +300,18 @@ int moe_prefill_forward(const float *x, int32_t t, const moe_router *router, moe
   pa.top_k = d.top_k;
   pa.t = t;
   pa.xh = reinterpret_cast<_Float16 *>(ws + L.pf_xh);
-  pa.act = reinterpret_cast<_Float16 *>(ws + L.pf_act);
+  pa.xg = reinterpret_cast<float *>(ws + L.pf_xg);
+  pa.act = reinterpret_cast<float *>(ws + L.pf_act);
   pa.y = reinterpret_cast<float *>(ws + L.pf_y);
+  pa.meta = reinterpret_cast<int32_t *>(ws + L.pf_meta);
   pa.status = reinterpret_cast<uint32_t *>(ws + L.counters) + kSyncStatus;
   pa.out = out;
-  if ((rc = launched(launch_prefill_experts(pa, s), "prefill experts"))) return rc;
-  if ((rc = stage_done(1, s))) return rc;
-  return ok();
+  rc = launched(launch_prefill(pa, router->weight, shared->gate, plan->logits, plan->gamma,
+                               plan->topk_idx, reinterpret_cast<uint32_t *>(ws + L.counters) + kSyncRoute,
+                               plan->expert_ptr, plan->entry_row, plan->entry_rank, s, g_stage_ev,
+                               g_stage_n),
+                "prefill");
+  return rc ? rc : ok();
 }
 
 int moe_workspace_status(void *ws, size_t ws_bytes, void *stream) {

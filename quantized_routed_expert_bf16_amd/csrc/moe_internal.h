@@ -98,9 +98,11 @@ struct WorkspaceLayout {
   size_t act;          // decode: [64][4][I] f32
   size_t opart;        // decode: [8][4][H] f32 per-slice partial outputs
   size_t slice_logits; // decode: [8][4][256] f64, [8][4] f32 gamma after it
-  size_t pf_xh;        // prefill: [32][H] f16 activations
-  size_t pf_act;       // prefill: [t*k + t][I] f16 activations per CSR entry
+  size_t pf_xh;        // prefill: [2][32][H] f16 hi/lo split of x
+  size_t pf_xg;        // prefill: [32][H/64] f32 group sums of x
+  size_t pf_act;       // prefill: [t*k + t][I] f32 act per entry
   size_t pf_y;         // prefill: [t][k+1][H] f32 weighted outputs per (row, rank)
+  size_t pf_meta;      // prefill: [1 + 256] i32 used experts
   size_t total;
 };
 
@@ -123,7 +125,6 @@ constexpr int kMaxDownTiles = 256;
 
 // ------------------------------------------------------------- launchers
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
-hipError_t launch_prefill_route(const RouteArgs &a, hipStream_t s);
 hipError_t launch_layer(const LayerLaunch &l, hipStream_t s);
 int decode_rows_per_tile(int inter);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
@@ -137,15 +138,21 @@ struct PrefillArgs {
   const int32_t *expert_ptr;   // [E+1]
   const int32_t *entry_row;    // [t*k]
   const int32_t *entry_rank;   // [t*k]
-  const float *topk_w;         // [t][k]
+  float *topk_w;               // [t][k]
   const float *gamma;          // [t]
   int hidden, inter, n_experts, top_k, t;
-  _Float16 *xh;                // [32][H]
-  _Float16 *act;               // [(t*k + t)][I]
-  float *y;                    // [t][k+1][H]
+  _Float16 *xh;                // [2][32][H]: f16 hi rows, then lo rows
+  float *xg;                   // [32][H/64] group sums of x
+  float *act;                  // [t*k + t][I] silu(g)*u per entry (shared entries last)
+  float *y;                    // [t][k+1][H] weighted output per (row, rank); rank k = shared
+  int32_t *meta;               // [1 + E]: used-expert count, then their ids ascending
   uint32_t *status;
   float *out;                  // [t][H]
 };
-hipError_t launch_prefill_experts(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs &a, const uint16_t *router, const uint16_t *gvec,
+                          double *logits, float *gamma, uint32_t *topk_idx, uint32_t *counter,
+                          int32_t *expert_ptr, int32_t *entry_row, int32_t *entry_rank,
+                          hipStream_t s, hipEvent_t *stage_ev, int n_ev);
+
 
 }  // namespace moe

@@ -1,11 +1,10 @@
-// Router matvec, top-k softmax, union / slot table (decode) and rows grouped
-// by expert (prefill), for gfx950.
+// Router matvec, top-k softmax, union and slot table of one decode step
+// (moe_route without the experts), for gfx950.
 //
 // Struct Gpu router_b: "softmax over experts, top-k" for nb rows; gpu.rs
 // union_of: "unique entries in first-seen order"; gpu.rs slot_tab / wmap field
 // docs: 64 descriptors per layer, entry 62 = resident count, 63 = union size,
-// per-row routing weight per slot; Struct Gpu prepare_expert_jobs: rows
-// grouped by expert in CSR row order.
+// per-row routing weight per slot.
 //
 // One launch does everything: every wave computes whole router rows (the E
 // expert rows plus the shared-gate vector as row E) with float64 accumulation
@@ -168,53 +167,6 @@ __global__ __launch_bounds__(kThreads) void route_decode_kernel(RouteArgs a) {
   if (threadIdx.x == 0) st_dev(a.counter, 0u);
 }
 
-__global__ __launch_bounds__(kThreads) void route_prefill_kernel(RouteArgs a) {
-  router_matvec(a);
-  if (!arrive_last(a.counter)) return;
-
-  constexpr int kRows = MOE_MAX_PREFILL_ROWS;
-  __shared__ double lg[kRows * kMaxExperts];
-  __shared__ int sel[kRows * kMaxTopK];
-  __shared__ float wsel[kRows * kMaxTopK];
-  __shared__ int cnt[kMaxExperts + 1];
-  const int E = a.n_experts, k = a.top_k, t = a.rows;
-  for (int p = threadIdx.x; p < t * E; p += kThreads) lg[p] = ld_dev(a.logits + p);
-  __syncthreads();
-  rank_topk(lg, t, E, k, sel);
-  __syncthreads();
-  topk_weights(a, lg, sel, wsel);
-
-  // CSR by expert: experts ascending, rows ascending (one thread per expert)
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    int c = 0;
-    for (int p = 0; p < t * k; ++p) c += (sel[(p / k) * kMaxTopK + p % k] == e);
-    cnt[e] = c;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) {
-      const int c = cnt[e];
-      cnt[e] = run;
-      run += c;
-    }
-    cnt[E] = run;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e <= E; e += kThreads) a.expert_ptr[e] = cnt[e];
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    int pos = cnt[e];
-    for (int r = 0; r < t; ++r)
-      for (int c = 0; c < k; ++c)
-        if (sel[r * kMaxTopK + c] == e) {
-          a.entry_row[pos] = r;
-          a.entry_rank[pos] = c;
-          ++pos;
-        }
-  }
-  if (threadIdx.x == 0) st_dev(a.counter, 0u);
-}
-
 __global__ void fill_zero_kernel(uint4 *p, size_t n16) {
   for (size_t i = blockIdx.x * size_t(blockDim.x) + threadIdx.x; i < n16;
        i += size_t(gridDim.x) * blockDim.x)
@@ -227,11 +179,6 @@ int route_blocks(int n_experts) { return (n_experts + 1 + kWaves - 1) / kWaves; 
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(route_decode_kernel, dim3(route_blocks(a.n_experts)), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_prefill_route(const RouteArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(route_prefill_kernel, dim3(route_blocks(a.n_experts)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
