@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="decode_nb1")
-    ap.add_argument("--extra", default="verify_nb4",
+    ap.add_argument("--extra", default="verify_nb4,lowbit_q3,lowbit_q2,mixed_q4q2,prefill_t32",
                     help="comma-separated further configurations reported under 'extra'")
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
     ap.add_argument("--chunk", type=int, default=25, help="steps per captured graph")
@@ -275,6 +275,172 @@ class HipEvents:
         self.ev = []
 
 
+class PrefillBench:
+    """Prefill chunks of 32 rows through all layers of the workload."""
+
+    def __init__(self, moe, torch, syn, cfg, chunks, warmup, seed):
+        import ctypes
+        self.moe, self.torch, self.cfg = moe, torch, cfg
+        self.chunks, self.warmup = chunks, warmup
+        t0 = time.time()
+        self.p = syn.make_problem(cfg, seed=seed, device="cuda")
+        self.x = syn.make_x(cfg, seed=seed + 1, steps=chunks + warmup, device="cuda", problem=self.p)
+        torch.cuda.synchronize()
+        log(f"{cfg.name}: pool {self.p.pool.numel() / 2**30:.2f} GiB generated in {time.time() - t0:.1f} s")
+        c = cfg
+        self.L = self.p.rec.shape[0]
+        self.t = c.nb
+        self.dims = moe.make_dims(c.hidden, c.inter, c.n_experts, c.top_k)
+        self.bufs = moe.PrefillBuffers(self.dims)
+        self.pool = moe.make_pool(self.p.pool)
+        self.routers = [moe.make_router(self.dims, self.p.router[l], self.p.rec[l]) for l in range(self.L)]
+        self.shared = [moe.make_shared(self.p.shared_gate[l], int(self.p.shared_rec[l]))
+                       for l in range(self.L)]
+        self.out = torch.zeros(self.L, self.t, c.hidden, dtype=torch.float32, device="cuda")
+        self.ct = ctypes
+        self.f = moe.lib.moe_prefill_forward
+        self.ref = {"plan": ctypes.byref(self.bufs.plan), "pool": ctypes.byref(self.pool),
+                    "routers": [ctypes.byref(r) for r in self.routers],
+                    "shared": [ctypes.byref(s) for s in self.shared]}
+        self.x_ptr = self.x.data_ptr()
+        self.x_step = self.x[0].numel() * 4
+        self.x_layer = self.x[0, 0].numel() * 4
+        self.out_ptr = [self.out[l].data_ptr() for l in range(self.L)]
+
+    def call(self, s, l, stream):
+        rc = self.f(self.x_ptr + s * self.x_step + l * self.x_layer, self.t, self.ref["routers"][l],
+                    self.ref["plan"], self.ref["pool"], self.ref["shared"][l], self.out_ptr[l], stream)
+        if rc:
+            raise self.moe.MoeError(rc, self.moe.last_error())
+
+    def csr_pass(self):
+        torch = self.torch
+        E = self.cfg.n_experts
+        ptrs = torch.zeros(self.chunks, self.L, E + 1, dtype=torch.int32, device="cuda")
+        st = torch.cuda.current_stream().cuda_stream
+        for s in range(self.chunks):
+            for l in range(self.L):
+                self.call(self.warmup + s, l, st)
+                ptrs[s, l].copy_(self.bufs.expert_ptr)
+        torch.cuda.synchronize()
+        return ptrs.cpu().numpy()
+
+    def costs(self, ptrs):
+        """Per (chunk, layer): algorithmic bytes, gate/up and down bytes, flops."""
+        import numpy as np
+        c, moe = self.cfg, self.moe
+        H, I, E = c.hidden, c.inter, c.n_experts
+        rec = self.p.rec.cpu().numpy()
+        bits_of = {0: 4, 1: 3, 2: 2}
+        rb = {b: moe.record_bytes(H, I, b) for b in (4, 3, 2)}
+        gu = {b: 2 * I * (H * b // 8) + 2 * I * (H // 64) * 4 for b in (4, 3, 2)}
+        cnt = np.diff(ptrs, axis=2)
+        total = np.zeros(cnt.shape[:2])
+        gu_b = np.zeros(cnt.shape[:2])
+        flops = np.zeros(cnt.shape[:2])
+        for s in range(cnt.shape[0]):
+            for l in range(cnt.shape[1]):
+                used = np.nonzero(cnt[s, l])[0]
+                bits = [bits_of[int(rec[l, e]) & 3] for e in used]
+                total[s, l] = sum(rb[b] for b in bits) + rb[4]
+                gu_b[s, l] = sum(gu[b] for b in bits) + gu[4]
+                rows = int(cnt[s, l].sum()) + self.t
+                flops[s, l] = 2.0 * rows * (2 * I * H + H * I)
+        other = E * H * 2 + H * 2 + 2 * self.t * H * 4
+        return cnt, total + other, gu_b, flops
+
+    def run_graph(self):
+        torch = self.torch
+        side = torch.cuda.Stream()
+        self.call(0, 0, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        wg, g = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(wg, stream=side):
+            sc = torch.cuda.current_stream().cuda_stream
+            for s in range(self.warmup):
+                for l in range(self.L):
+                    self.call(s, l, sc)
+        with torch.cuda.graph(g, stream=side):
+            sc = torch.cuda.current_stream().cuda_stream
+            for s in range(self.chunks):
+                for l in range(self.L):
+                    self.call(self.warmup + s, l, sc)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            wg.replay()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    def stage_pass(self, n_chunks):
+        moe = self.moe
+        n_chunks = min(n_chunks, self.chunks)
+        n = n_chunks * self.L
+        ev = HipEvents(5 * n)
+        arr_t = self.ct.c_void_p * 4
+        st = self.torch.cuda.current_stream().cuda_stream
+        i = 0
+        for s in range(n_chunks):
+            for l in range(self.L):
+                rc = moe.lib.moe_set_stage_events(arr_t(*ev.ev[5 * i + 1: 5 * i + 5]), 4)
+                if rc:
+                    raise moe.MoeError(rc, moe.last_error())
+                ev.record(5 * i, st)
+                self.call(self.warmup + s, l, st)
+                i += 1
+        moe.lib.moe_set_stage_events(None, 0)
+        self.torch.cuda.synchronize()
+        names = ("route_topk_csr", "gate_up", "down", "combine")
+        per = {nm: [ev.ms(5 * q + j, 5 * q + j + 1) * 1e3 for q in range(n)] for j, nm in enumerate(names)}
+        ev.close()
+        return n_chunks, per
+
+
+def bench_prefill(moe, torch, syn, name, args):
+    import numpy as np
+    cfg = syn.CONFIGS[name]
+    b = PrefillBench(moe, torch, syn, cfg, cfg.steps, 2, args.seed)
+    log(f"{name}: CSR pass")
+    ptrs = b.csr_pass()
+    cnt, all_b, gu_b, flops = b.costs(ptrs)
+    log(f"{name}: timed pass (graph)")
+    total_ms = b.run_graph()
+    n_calls = cfg.steps * b.L
+    us_call = total_ms * 1e3 / n_calls
+    total_s = total_ms / 1e3
+    log(f"{name}: {us_call:.2f} us per chunk-layer, {all_b.sum() / total_s / 1e9:.0f} GB/s")
+    n_st, per = b.stage_pass(4)
+    gu_us = statistics.mean(per["gate_up"])
+    gu_gbs = float(gu_b[:n_st].mean()) / (gu_us * 1e-6) / 1e9
+    down_us = statistics.mean(per["down"])
+    used = (cnt > 0).sum(axis=2)
+    out = {
+        "config": name, "description": cfg.description, "rows_per_chunk": b.t, "layers": b.L,
+        "chunks": cfg.steps, "mode": "graph",
+        "us_per_chunk_layer": us_call,
+        "us_per_token_layer": us_call / b.t,
+        "tokens_per_s": b.t * cfg.steps / total_s,
+        "all_bytes_gbs": float(all_b.sum() / total_s / 1e9),
+        "hbm_frac": float(all_b.sum() / total_s / 1e9 / HBM_PEAK_GBS),
+        "mfma_tflops": float(flops.sum() / total_s / 1e12),
+        "mfma_frac_f16_dense": float(flops.sum() / total_s / 1e12 / 2500.0),
+        "experts_used_mean": float(used.mean()), "experts_used_min": int(used.min()),
+        "experts_used_max": int(used.max()),
+        "stage_us_mean": {k_: statistics.mean(v) for k_, v in per.items()},
+        "gate_up_gbs": gu_gbs, "gate_up_hbm_frac": gu_gbs / HBM_PEAK_GBS,
+        "gate_up_tflops": float(flops[:n_st].mean() * 2 / 3 / (gu_us * 1e-6) / 1e12),
+        "down_us_mean": down_us,
+    }
+    del b
+    torch.cuda.empty_cache()
+    return out
+
+
 def pct(v, q):
     v = sorted(v)
     return v[min(len(v) - 1, int(q * (len(v) - 1) + 0.5))]
@@ -393,7 +559,10 @@ def main():
     main_res = bench_decode(moe, torch, syn, args.config, args, with_cpu=not args.no_cpu)
     extra = {}
     for name in [n for n in args.extra.split(",") if n]:
-        extra[name] = bench_decode(moe, torch, syn, name, args, with_cpu=False)
+        if syn.CONFIGS[name].prefill:
+            extra[name] = bench_prefill(moe, torch, syn, name, args)
+        else:
+            extra[name] = bench_decode(moe, torch, syn, name, args, with_cpu=False)
     line = {
         "metric": METRIC,
         "value": round(main_res["expert_weight_gbs"], 2),
