@@ -189,6 +189,50 @@ __device__ inline double readlane_d(double v, int lane) {
   const uint32_t hi = __builtin_amdgcn_readlane(int(uint32_t(u >> 32)), lane);
   return __longlong_as_double((uint64_t(hi) << 32) | lo);
 }
+// Order-preserving u64 key of a finite double (larger double <-> larger key).
+__device__ inline uint64_t order_key(double v) {
+  const uint64_t b = __double_as_longlong(v);
+  return (b >> 63) ? ~b : (b | (uint64_t(1) << 63));
+}
+template <int CTRL>
+__device__ inline uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_mov_dpp(int(uint32_t(v)), CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp(int(uint32_t(v >> 32)), CTRL, 0xF, 0xF, true);
+  return (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
+}
+__device__ inline uint64_t readlane_u64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane(int(uint32_t(v)), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(int(uint32_t(v >> 32)), lane);
+  return (uint64_t(hi) << 32) | lo;
+}
+// (key, id) pairs ordered by key descending, then id ascending.
+__device__ inline bool pair_before(uint64_t ka, int ia, uint64_t kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+template <int CTRL>
+__device__ inline void argmax_step(uint64_t &k, int &i) {
+  const uint64_t ok = dpp_u64<CTRL>(k);
+  const int oi = __builtin_amdgcn_mov_dpp(i, CTRL, 0xF, 0xF, true);
+  if (pair_before(ok, oi, k, i)) { k = ok; i = oi; }
+}
+// Wave-wide best (key, id); the result is uniform.
+__device__ inline void wave_argmax(uint64_t &k, int &i) {
+  argmax_step<0xB1>(k, i);
+  argmax_step<0x4E>(k, i);
+  argmax_step<0x141>(k, i);
+  argmax_step<0x140>(k, i);
+  uint64_t bk = readlane_u64(k, 0);
+  int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+  for (int r = 16; r < 64; r += 16) {
+    const uint64_t ck = readlane_u64(k, r);
+    const int ci = __builtin_amdgcn_readlane(i, r);
+    if (pair_before(ck, ci, bk, bi)) { bk = ck; bi = ci; }
+  }
+  k = bk;
+  i = bi;
+}
+
 __device__ inline double wave_sum_d(double v) {
   v += dpp_d<kDppXor1>(v);
   v += dpp_d<kDppXor2>(v);

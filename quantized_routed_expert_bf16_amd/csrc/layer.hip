@@ -46,7 +46,7 @@ constexpr int kPairsPerWave = kTileRowPairs / kWaves;
 constexpr int kRowsPerWave = 8;                       // down unit: 8 rows per wave
 constexpr int kRowsPerTile = kRowsPerWave * kWaves;   // 32 rows per down tile
 constexpr int kSlotBatch = 10;                        // slots per lane per down batch
-constexpr int kStageCols = 256;                       // slot-groups x slice width, per batch
+constexpr int kStageCols = 256;                       // slot groups x slice width (= 8 x 32)
 constexpr uint32_t kSpinLimit = 1u << 22;
 
 struct LayerArgs {
@@ -80,7 +80,7 @@ __device__ inline void wait_geq(const LayerArgs &a, const uint32_t *p, uint32_t 
           break;
         }
       }
-      __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_s_sleep(4);
     }
   }
   __syncthreads();
@@ -94,6 +94,9 @@ struct Shared {
   int uid[kSlotStride];
   float wslot[NB][kSlotStride];   // routing weight per slot (index u: gamma)
   uint64_t desc[kSlotStride];     // descriptor per slot (index u: shared expert)
+  const uint8_t *dcodes[kSlotStride];   // down codes of the slot's record (null: skip)
+  const uint32_t *dsb[kSlotStride];     // down (scale, bias) words
+  int dbits[kSlotStride];               // bit width (0: bad descriptor)
   float gam[NB];
   int u;
   uint32_t prev;
@@ -136,83 +139,100 @@ __device__ void router_rows(const LayerArgs &a, const float *xs, int lr, double 
 }
 
 // Top-k, weights and union of the slice's published logits (every block).
-// The rank of expert e in row b is the number of experts ordered before it
-// by (logit descending, id ascending); every thread ranks its experts against
-// the whole row, read two logits at a time as LDS broadcasts.  Lanes < k of
-// wave b take one exp each for the softmax; the union is one ballot.
+// Wave b ranks row b: k rounds of a wave-wide argmax over order-preserving
+// 64-bit keys of the float64 logits (ties to the lower id), DPP inside
+// 16-lane rows and readlane across rows; lanes < k then take one exp each
+// for the softmax.  Wave 0 builds the first-seen union with readlane
+// broadcasts and the per-slot record pointers used by the expert units.
 template <int NB>
 __device__ void build_routing(const LayerArgs &a, Shared<NB> &s, const double *lg, const float *gm,
-                              const uint64_t *rec_lds, double *lgs) {
+                              const uint64_t *rec_lds, uint64_t *lkey, double *lval) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int E = a.l.n_experts, k = a.l.top_k;
-  const int Ep = (E + 7) & ~7;    // rows padded to a multiple of 8 with -inf
+  // order-preserving keys of the row logits in LDS (value kept for softmax)
+  const int Ep = (E + 7) & ~7;
   for (int p = threadIdx.x; p < NB * Ep; p += kThreads) {
     const int b = p / Ep, e = p - b * Ep;
-    lgs[b * Ep + e] = e < E ? ld_dev(lg + b * kMaxExperts + e) : -__builtin_inf();
+    // + 0.0 folds -0 into +0 so that equal logits tie on the id alone
+    const double v = e < E ? ld_dev(lg + b * kMaxExperts + e) + 0.0 : 0.0;
+    lkey[b * Ep + e] = e < E ? order_key(v) : 0;
+    lval[b * Ep + e] = v;
   }
   if (threadIdx.x < NB) s.gam[threadIdx.x] = ld_dev(gm + threadIdx.x);
-  for (int p = threadIdx.x; p < NB * kMaxTopK; p += kThreads) s.sel[p / kMaxTopK][p % kMaxTopK] = 0;
   __syncthreads();
-  for (int p = threadIdx.x; p < NB * E; p += kThreads) {
-    const int b = p / E, e = p - b * E;
-    const double v = lgs[b * Ep + e];
-    const double2 *row = reinterpret_cast<const double2 *>(lgs + b * Ep);
-    int rank = 0;
-    // branch-free: four broadcast reads in flight per step
-    for (int f2 = 0; f2 < Ep / 2; f2 += 4) {
-      const double2 o0 = row[f2], o1 = row[f2 + 1], o2 = row[f2 + 2], o3 = row[f2 + 3];
-      const int f = 2 * f2;
-      rank += int(o0.x > v) + int(o0.y > v) + int(o1.x > v) + int(o1.y > v) +
-              int(o2.x > v) + int(o2.y > v) + int(o3.x > v) + int(o3.y > v);
-      rank += (int(o0.x == v) & int(f < e)) + (int(o0.y == v) & int(f + 1 < e)) +
-              (int(o1.x == v) & int(f + 2 < e)) + (int(o1.y == v) & int(f + 3 < e)) +
-              (int(o2.x == v) & int(f + 4 < e)) + (int(o2.y == v) & int(f + 5 < e)) +
-              (int(o3.x == v) & int(f + 6 < e)) + (int(o3.y == v) & int(f + 7 < e));
+  // exact rank of every (row, expert): experts before it by (key desc, id
+  // asc).  S adjacent lanes split the compare range and merge with DPP.
+  const int items = NB * E;
+  const int S = items <= kThreads / 4 ? 4 : (items <= kThreads / 2 ? 2 : 1);
+  for (int base = 0; base < items * S; base += kThreads) {
+    const int t = base + threadIdx.x;
+    const int p = t / S, h = t % S;
+    int rank = 0, b = 0, e = 0;
+    if (p < items) {
+      b = p / E;
+      e = p - b * E;
+      const uint64_t key = lkey[b * Ep + e];
+      const uint64_t *row = lkey + b * Ep;
+      const int span = Ep / S, f0 = h * span;
+      for (int f = f0; f < f0 + span; f += 2) {
+        const uint64_t o0 = row[f], o1 = row[f + 1];
+        rank += int(o0 > key) + int(o1 > key) + (int(o0 == key) & int(f < e)) +
+                (int(o1 == key) & int(f + 1 < e));
+      }
     }
-    if (rank < k) {
+    if (S >= 2) rank += __builtin_amdgcn_mov_dpp(rank, 0xB1, 0xF, 0xF, true);   // xor 1
+    if (S >= 4) rank += __builtin_amdgcn_mov_dpp(rank, 0x4E, 0xF, 0xF, true);   // xor 2
+    if (p < items && h == 0 && rank < k) {
       s.sel[b][rank] = e;
-      s.selv[b][rank] = v;
+      s.selv[b][rank] = lval[b * Ep + e];
     }
   }
   __syncthreads();
   if (wave < NB) {
     const int b = wave;
-    double ex = 0.0;
-    if (lane < k) ex = exp(s.selv[b][lane] - s.selv[b][0]);
+    const double ex = lane < k ? exp(s.selv[b][lane] - s.selv[b][0]) : 0.0;
     const double sum = wave_sum_d(ex);
     if (lane < k) s.wsel[b][lane] = float(ex / sum);
   }
+  __syncthreads();
   if (wave == 0) {
-    // first-seen union over the row-major (row, rank) list
+    // first-seen union over the row-major (row, rank) list, lane p = entry p
     const int n = NB * k;
-    int e = -1, first = 0;
-    if (lane < n) {
-      e = s.sel[lane / k][lane % k];
-      first = 1;
-      for (int q = 0; q < lane; ++q) first &= (s.sel[q / k][q % k] != e);
+    const int e = lane < n ? s.sel[lane / k][lane % k] : -1;
+    int first = lane < n;
+    for (int q = 0; q < n; ++q) {
+      const int eq = __builtin_amdgcn_readlane(e, q);
+      first &= !(q < lane && eq == e);
     }
     const uint64_t mask = __ballot(first);
     const int slot = __popcll(mask & ((uint64_t(1) << lane) - 1));
+    const int u = __popcll(mask);
     if (first) s.uid[slot] = e;
-    if (lane == 0) s.u = __popcll(mask);
-  }
-  __syncthreads();
-  const int u = s.u;
-  for (int j = threadIdx.x; j < kSlotStride; j += kThreads) {
-    s.desc[j] = j < u ? rec_lds[s.uid[j]] : (j == u ? a.l.shared_rec : 0);
+    if (lane == 0) s.u = u;
+    __builtin_amdgcn_wave_barrier();
+    // per-slot descriptor and routing weight of every row; slot u = shared
+    const int j = lane;
+    const int ej = j < u ? s.uid[j] : -1;
+    const uint64_t dj = j < u ? rec_lds[ej] : (j == u ? a.l.shared_rec : 0);
+    s.desc[j] = dj;
+    {
+      const bool ok = j <= u && record_ok(dj, a.l.pool_bytes, a.l.hidden, a.l.inter);
+      const int bt = ok ? bits_of_tag(dj) : 0;
+      const RecordLayout L = record_layout(a.l.hidden, a.l.inter, ok ? bt : 4);
+      const uint8_t *rec = a.l.pool + (dj & ~uint64_t(255));
+      s.dbits[j] = bt;
+      s.dcodes[j] = ok ? rec + L.d_codes : nullptr;
+      s.dsb[j] = ok ? reinterpret_cast<const uint32_t *>(rec + L.d_sb) : nullptr;
+    }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       float w = 0.0f;
-      if (j < u) {
-        for (int r = 0; r < k; ++r)
-          if (s.sel[b][r] == s.uid[j]) w = s.wsel[b][r];
-      } else if (j == u) {
-        w = s.gam[b];
-      }
-      s.wslot[b][j] = w;
+      for (int r = 0; r < k; ++r) w = (s.sel[b][r] == ej) ? s.wsel[b][r] : w;
+      s.wslot[b][j] = j < u ? w : (j == u ? s.gam[b] : 0.0f);
     }
   }
   __syncthreads();
+  const int u = s.u;
   if (blockIdx.x == 0) {   // caller-visible routing tables
     for (int j = threadIdx.x; j < kSlotStride; j += kThreads) {
       a.l.ids[j] = j < u ? uint32_t(s.uid[j]) : 0u;
@@ -225,7 +245,8 @@ __device__ void build_routing(const LayerArgs &a, Shared<NB> &s, const double *l
       a.l.topk_idx[p] = uint32_t(s.sel[p / k][p % k]);
       a.l.topk_w[p] = s.wsel[p / k][p % k];
     }
-    for (int p = threadIdx.x; p < NB * E; p += kThreads) a.l.logits[p] = lgs[(p / E) * Ep + p % E];
+    for (int p = threadIdx.x; p < NB * E; p += kThreads)
+      a.l.logits[p] = ld_dev(lg + (p / E) * kMaxExperts + p % E);
     if (threadIdx.x < NB) a.l.gamma[threadIdx.x] = s.gam[threadIdx.x];
   }
 }
@@ -333,7 +354,8 @@ __device__ void run_gate_up(const LayerArgs &a, int x, uint64_t desc, int act_sl
 // A down tile: 32 output rows of the slice's columns, every slot.  Lane
 // (row rw, chunk c, slot group g) of a wave handles row rw, 32-code chunk c
 // of the slice, and slots g, g + SG, ...; weights for the lane's slots are
-// loaded before the wait for the slice's gate/up units.
+// loaded before the wait for the slice's gate/up units, the act chunks with
+// device-coherent loads after it.
 template <int NB>
 __device__ void run_down(const LayerArgs &a, Shared<NB> &sh, int x, int tile, float *act_lds,
                          float *asum_lds) {
@@ -355,61 +377,53 @@ __device__ void run_down(const LayerArgs &a, Shared<NB> &sh, int x, int tile, fl
     // 1. this lane's weights for the batch
     uint32_t w[kSlotBatch][4];
     uint32_t sbw[kSlotBatch];
-    int bits[kSlotBatch];
 #pragma unroll
     for (int m = 0; m < kSlotBatch; ++m) {
       const int slot = s0 + g + sg * m;
-      bits[m] = 0;
       w[m][0] = w[m][1] = w[m][2] = w[m][3] = 0;
       sbw[m] = 0;
-      if (slot < n_slots) {
-        const uint64_t desc = sh.desc[slot];
-        if (record_ok(desc, a.l.pool_bytes, H, I)) {
-          const int bt = bits_of_tag(desc);
-          const RecordLayout L = record_layout(H, I, bt);
-          const uint8_t *rec = a.l.pool + (desc & ~uint64_t(255));
-          const uint8_t *grow = rec + L.d_codes + (size_t(grp) * H + row) * (kGroup * bt / 8);
-          if (bt == 4) load_chunk<4>(grow, kGroup, half, w[m]);
-          else if (bt == 3) load_chunk<3>(grow, kGroup, half, w[m]);
-          else load_chunk<2>(grow, kGroup, half, w[m]);
-          sbw[m] = reinterpret_cast<const uint32_t *>(rec + L.d_sb)[size_t(grp) * H + row];
-          bits[m] = bt;
-        } else if (rw == 0 && c == 0) {
-          set_status(a, 1u);
-        }
+      const int bt = slot < n_slots ? sh.dbits[slot] : 0;
+      if (bt) {
+        const uint8_t *grow = sh.dcodes[slot] + (size_t(grp) * H + row) * (kGroup * bt / 8);
+        if (bt == 4) load_chunk<4>(grow, kGroup, half, w[m]);
+        else if (bt == 3) load_chunk<3>(grow, kGroup, half, w[m]);
+        else load_chunk<2>(grow, kGroup, half, w[m]);
+        sbw[m] = sh.dsb[slot][size_t(grp) * H + row];
       }
     }
     // 2. the slice's act values must be complete
     if (s0 == 0) wait_geq(a, sw(a, x, kSliceGu), uint32_t(n_slots * a.ups));
-    // 3. stage the batch's act (slice columns) and per-chunk sums in LDS
+    // 3. stage the batch's act chunks in LDS: one device-coherent 16-byte
+    //    load per thread; 8 consecutive threads hold one 32-value chunk and
+    //    form its sum with a DPP group-of-8 reduction
     const int nb_slots = min(n_slots - s0, sg * kSlotBatch);
+    const int n_f4 = nb_slots * NB * (W / 4);
     __syncthreads();
-    for (int i = threadIdx.x; i < nb_slots * NB * (W / 4); i += kThreads) {
-      const int q = i % (W / 4), b = (i / (W / 4)) % NB, sl = i / (W / 4) / NB;
-      const int slot = s0 + sl;
-      const int ps = slot < u ? slot : kSharedSlot;
-      const float *src = a.l.act + (size_t(ps) * kMaxNb + b) * I + x * W + 4 * q;
-      *reinterpret_cast<float4 *>(act_lds + (sl * NB + b) * W + 4 * q) = ld_dev_f4(src);
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < nb_slots * NB * cpr; i += kThreads) {
-      const float *p = act_lds + (i / cpr) * W + (i % cpr) * kChunk;
-      float sm = 0.0f;
-#pragma unroll
-      for (int t = 0; t < kChunk; ++t) sm += p[(t + i) & (kChunk - 1)];   // no bank conflicts
-      asum_lds[i] = sm;
+    for (int i0 = 0; i0 < n_f4; i0 += kThreads) {
+      const int i = i0 + threadIdx.x;
+      float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < n_f4) {
+        const int q = i % (W / 4), b = (i / (W / 4)) % NB, sl = i / (W / 4) / NB;
+        const int slot = s0 + sl;
+        const int ps = slot < u ? slot : kSharedSlot;
+        f = ld_dev_f4(a.l.act + (size_t(ps) * kMaxNb + b) * I + x * W + 4 * q);
+        *reinterpret_cast<float4 *>(act_lds + (sl * NB + b) * W + 4 * q) = f;
+      }
+      const float cs = group8_sum((f.x + f.y) + (f.z + f.w));   // i = 8 * chunk + (0..7)
+      if (i < n_f4 && (i & 7) == 0) asum_lds[i >> 3] = cs;
     }
     __syncthreads();
     // 4. accumulate the lane's slots
 #pragma unroll
     for (int m = 0; m < kSlotBatch; ++m) {
-      if (bits[m] == 0) continue;
       const int sl = g + sg * m;
       const int slot = s0 + sl;
+      const int bt = slot < n_slots ? sh.dbits[slot] : 0;
+      if (bt == 0) continue;
       float P[NB];
       const LdsX ax{act_lds + sl * NB * W + c * kChunk, W};
-      if (bits[m] == 4) chunk_dot<4, NB>(w[m], ax, P);
-      else if (bits[m] == 3) chunk_dot<3, NB>(w[m], ax, P);
+      if (bt == 4) chunk_dot<4, NB>(w[m], ax, P);
+      else if (bt == 3) chunk_dot<3, NB>(w[m], ax, P);
       else chunk_dot<2, NB>(w[m], ax, P);
       const float sc = sb_scale(sbw[m]), bi = sb_bias(sbw[m]);
 #pragma unroll
@@ -444,11 +458,15 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
   __shared__ Shared<NB> sh;
   __shared__ uint64_t rec_lds[kMaxExperts];
   const int H = a.l.hidden;
+  // x and its sums live until the block's last gate/up unit; a block takes
+  // its down tiles after all of its gate/up units, so the act staging of the
+  // down tiles reuses that space.  The logit keys sit past x: the routing
+  // build runs between the shared and the routed gate/up units.
   float *xs = reinterpret_cast<float *>(dyn);           // [NB][H]
   float *xsum = xs + NB * H;                            // [NB][H/32]
-  float *act_lds = xsum + NB * (H / kChunk);            // [batch slots][NB][W]; logits first
-  static_assert(kStageCols * kSlotBatch >= 2 * kMaxExperts, "logits scratch must fit");
-  float *asum_lds = act_lds + kStageCols * kSlotBatch * NB;
+  float *keys = xsum + NB * (H / kChunk);               // [NB][E] key, [NB][E] value
+  float *act_lds = xs;                                  // [batch slots][NB][W]
+  float *asum_lds = act_lds + kStageCols * kSlotBatch * NB;   // [batch slots][NB][W/32]
 
   const int x = blockIdx.x % kSlices, lr = blockIdx.x / kSlices;
   const int P = a.per_slice;
@@ -478,8 +496,8 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
       run_gate_up<NB, CPL>(a, x, a.l.shared_rec, kSharedSlot, i, xs, xsum);
 
     wait_geq(a, sw(a, x, kSliceRoute), uint32_t(a.route_blocks));
-    // the logits scratch lives in the (not yet used) act staging area
-    build_routing<NB>(a, sh, lg, gm, rec_lds, reinterpret_cast<double *>(act_lds));
+    build_routing<NB>(a, sh, lg, gm, rec_lds, reinterpret_cast<uint64_t *>(keys),
+                      reinterpret_cast<double *>(keys) + NB * kMaxExperts);
     const int u = sh.u;
     const int n_gu = u * a.ups;
     const int n_total = n_gu + a.tiles;
@@ -507,9 +525,12 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
 }
 
 size_t dyn_lds_bytes(int nb, int hidden) {
-  // x, per-32 sums of x, one batch of staged act values, their per-chunk sums
-  return sizeof(float) * (size_t(nb) * hidden + size_t(nb) * (hidden / kChunk) +
-                          size_t(kStageCols) * kSlotBatch * nb + size_t(8) * kSlotBatch * nb);
+  // x, its per-32 sums and the logit keys; or one batch of staged act chunks
+  // and their sums
+  const size_t xk = sizeof(float) * (size_t(nb) * hidden + size_t(nb) * (hidden / kChunk)) +
+                    2 * sizeof(double) * size_t(nb) * kMaxExperts;
+  const size_t st = sizeof(float) * (size_t(kStageCols) * kSlotBatch * nb + size_t(8) * kSlotBatch * nb);
+  return xk > st ? xk : st;
 }
 
 struct LaunchCache {
