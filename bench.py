@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="N",
+                    help="first run N plain 1 GiB device copies (calibrates HBM byte counters)")
     return ap.parse_args()
 
 
@@ -556,6 +558,15 @@ def main():
     import synthetic as syn
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
+    if args.copy_probe:
+        n = 1 << 30
+        src = torch.full((n,), 1, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.copy_probe):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {args.copy_probe} copies of {n} bytes")
+        del src, dst
     main_res = bench_decode(moe, torch, syn, args.config, args, with_cpu=not args.no_cpu)
     extra = {}
     for name in [n for n in args.extra.split(",") if n]:
@@ -577,7 +588,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{main_res['config']}: {main_res['description']}, "
-                               f"{main_res['layers']} layers, fresh x per layer",
+                               f"fresh x per layer",
                    "nb": main_res["nb"], "layers": main_res["layers"], "mode": args.mode},
         "us_per_layer": round(main_res["us_per_layer_median"], 3),
         "us_per_layer_p90": round(main_res["us_per_layer_p90"], 3),

@@ -88,6 +88,8 @@ __device__ inline void wait_geq(const LayerArgs &a, const uint32_t *p, uint32_t 
 
 template <int NB>
 struct Shared {
+  double exq[64];
+  int ncand;
   int sel[NB][kMaxTopK];
   double selv[NB][kMaxTopK];
   float wsel[NB][kMaxTopK];
@@ -103,17 +105,44 @@ struct Shared {
 };
 
 // ----------------------------------------------------------------- route
-template <int NB>
-__device__ void router_rows(const LayerArgs &a, const float *xs, int lr, double *lg, float *gm) {
+// A wave's first router row (or the shared-expert gate vector, row E), loaded
+// into registers before the block stages x so that both loads overlap.
+template <int CPL>
+struct RouterRow {
+  uint4 w[4 * CPL];   // lane's 8 bf16 at inputs 8 lane + 512 t
+};
+
+template <int CPL>
+__device__ void router_prefetch(const LayerArgs &a, int lr, RouterRow<CPL> &r) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int H = a.l.hidden, E = a.l.n_experts;
+  const int e = lr * kWaves + wave;
+  if (e > E) return;
+  const uint16_t *w = e < E ? a.l.router + size_t(e) * H : a.l.gvec;
+#pragma unroll
+  for (int t = 0; t < 4 * CPL; ++t)
+    if (lane * 8 + 512 * t < H) r.w[t] = *reinterpret_cast<const uint4 *>(w + lane * 8 + 512 * t);
+}
+
+// Router logits (float64 accumulation of the bf16 weights times x) of rows
+// e = lr * 4 + wave, e += 4 P; row E is the shared expert's gate, stored as
+// its sigmoid.
+template <int NB, int CPL>
+__device__ void router_rows(const LayerArgs &a, const float *xs, int lr, const RouterRow<CPL> &first,
+                            double *lg, float *gm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int H = a.l.hidden, E = a.l.n_experts;
   for (int e = lr * kWaves + wave; e <= E; e += a.per_slice * kWaves) {
     const uint16_t *w = e < E ? a.l.router + size_t(e) * H : a.l.gvec;
+    const bool pre = e == lr * kWaves + wave;
     double acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = 0.0;
-    for (int i0 = lane * 8; i0 < H; i0 += 512) {
-      const uint4 wv = *reinterpret_cast<const uint4 *>(w + i0);
+#pragma unroll
+    for (int t = 0; t < 4 * CPL; ++t) {
+      const int i0 = lane * 8 + 512 * t;
+      if (i0 >= H) break;
+      const uint4 wv = pre ? first.w[t] : *reinterpret_cast<const uint4 *>(w + i0);
       const float wf[8] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y),
                            bf16_lo(wv.z), bf16_hi(wv.z), bf16_lo(wv.w), bf16_hi(wv.w)};
 #pragma unroll
@@ -122,7 +151,7 @@ __device__ void router_rows(const LayerArgs &a, const float *xs, int lr, double 
         const float4 x1 = *reinterpret_cast<const float4 *>(xs + b * H + i0 + 4);
         const float xf[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc[b] = fma(double(wf[t]), double(xf[t]), acc[b]);
+        for (int q = 0; q < 8; ++q) acc[b] = fma(double(wf[q]), double(xf[q]), acc[b]);
       }
     }
 #pragma unroll
@@ -139,96 +168,150 @@ __device__ void router_rows(const LayerArgs &a, const float *xs, int lr, double 
 }
 
 // Top-k, weights and union of the slice's published logits (every block).
-// Wave b ranks row b: k rounds of a wave-wide argmax over order-preserving
-// 64-bit keys of the float64 logits (ties to the lower id), DPP inside
-// 16-lane rows and readlane across rows; lanes < k then take one exp each
-// for the softmax.  Wave 0 builds the first-seen union with readlane
-// broadcasts and the per-slot record pointers used by the expert units.
+// The order is (logit descending, id ascending) on 64-bit order-preserving
+// keys of the float64 logits.  Step 1 counts, for every (row, expert), the
+// experts of its row with a larger high key word (32-bit compares, split
+// over adjacent lanes and merged with DPP); only entries with fewer than k
+// such experts can be selected, and any two entries whose high words tie
+// are both among them.  Step 2 (wave 0) completes the exact rank of those
+// candidates against each other, then takes the softmax of each row's k
+// selected logits, the first-seen union of the (row, rank) list and the
+// per-slot record pointers used by the expert units.
 template <int NB>
 __device__ void build_routing(const LayerArgs &a, Shared<NB> &s, const double *lg, const float *gm,
-                              const uint64_t *rec_lds, uint64_t *lkey, double *lval) {
+                              const uint64_t *rec_lds, uint8_t *kbuf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int E = a.l.n_experts, k = a.l.top_k;
-  // order-preserving keys of the row logits in LDS (value kept for softmax)
-  const int Ep = (E + 7) & ~7;
+  const int Ep = (E + 15) & ~15;
+  uint64_t *key = reinterpret_cast<uint64_t *>(kbuf);                       // [NB][Ep]
+  double *val = reinterpret_cast<double *>(kbuf) + NB * kMaxExperts;        // [NB][Ep]
+  uint32_t *khi = reinterpret_cast<uint32_t *>(val + NB * kMaxExperts);     // [NB][Ep]
+  int *cand = reinterpret_cast<int *>(khi + NB * kMaxExperts);              // candidate position
+  int *cgt = cand + NB * kMaxExperts;                                       // its step-1 count
   for (int p = threadIdx.x; p < NB * Ep; p += kThreads) {
     const int b = p / Ep, e = p - b * Ep;
-    // + 0.0 folds -0 into +0 so that equal logits tie on the id alone
+    // + 0.0 folds -0 into +0 so that equal logits tie on the id alone;
+    // padding keys are 0, below every finite logit's key
     const double v = e < E ? ld_dev(lg + b * kMaxExperts + e) + 0.0 : 0.0;
-    lkey[b * Ep + e] = e < E ? order_key(v) : 0;
-    lval[b * Ep + e] = v;
+    const uint64_t kk = e < E ? order_key(v) : 0;
+    key[p] = kk;
+    val[p] = v;
+    khi[p] = uint32_t(kk >> 32);
   }
   if (threadIdx.x < NB) s.gam[threadIdx.x] = ld_dev(gm + threadIdx.x);
+  if (threadIdx.x == 0) s.ncand = 0;
   __syncthreads();
-  // exact rank of every (row, expert): experts before it by (key desc, id
-  // asc).  S adjacent lanes split the compare range and merge with DPP.
+
+  // step 1: S = 2^lg_s adjacent lanes per entry, each over Ep / S keys
   const int items = NB * E;
-  const int S = items <= kThreads / 4 ? 4 : (items <= kThreads / 2 ? 2 : 1);
-  for (int base = 0; base < items * S; base += kThreads) {
+  const int lg_s = 4 * items <= kThreads ? 2 : (2 * items <= kThreads ? 1 : 0);
+  const int quads = (Ep >> lg_s) >> 2;
+  for (int base = 0; base < (items << lg_s); base += kThreads) {
     const int t = base + threadIdx.x;
-    const int p = t / S, h = t % S;
-    int rank = 0, b = 0, e = 0;
+    const int p = t >> lg_s, h = t & ((1 << lg_s) - 1);
+    int gt = 0, b = 0, e = 0;
     if (p < items) {
       b = p / E;
       e = p - b * E;
-      const uint64_t key = lkey[b * Ep + e];
-      const uint64_t *row = lkey + b * Ep;
-      const int span = Ep / S, f0 = h * span;
-      for (int f = f0; f < f0 + span; f += 2) {
-        const uint64_t o0 = row[f], o1 = row[f + 1];
-        rank += int(o0 > key) + int(o1 > key) + (int(o0 == key) & int(f < e)) +
-                (int(o1 == key) & int(f + 1 < e));
+      const uint32_t kh = khi[b * Ep + e];
+      const uint4 *row = reinterpret_cast<const uint4 *>(khi + b * Ep) + h * quads;
+#pragma unroll 8
+      for (int f = 0; f < quads; ++f) {
+        const uint4 o = row[f];
+        gt += (int(o.x > kh) + int(o.y > kh)) + (int(o.z > kh) + int(o.w > kh));
       }
     }
-    if (S >= 2) rank += __builtin_amdgcn_mov_dpp(rank, 0xB1, 0xF, 0xF, true);   // xor 1
-    if (S >= 4) rank += __builtin_amdgcn_mov_dpp(rank, 0x4E, 0xF, 0xF, true);   // xor 2
-    if (p < items && h == 0 && rank < k) {
-      s.sel[b][rank] = e;
-      s.selv[b][rank] = lval[b * Ep + e];
+    if (lg_s >= 1) gt += __builtin_amdgcn_mov_dpp(gt, 0xB1, 0xF, 0xF, true);   // xor 1
+    if (lg_s >= 2) gt += __builtin_amdgcn_mov_dpp(gt, 0x4E, 0xF, 0xF, true);   // xor 2
+    if (p < items && h == 0 && gt < k) {
+      const int j = atomicAdd(&s.ncand, 1);
+      cand[j] = b * Ep + e;
+      cgt[j] = gt;
     }
   }
   __syncthreads();
-  if (wave < NB) {
-    const int b = wave;
-    const double ex = lane < k ? exp(s.selv[b][lane] - s.selv[b][0]) : 0.0;
-    const double sum = wave_sum_d(ex);
-    if (lane < k) s.wsel[b][lane] = float(ex / sum);
-  }
-  __syncthreads();
+
   if (wave == 0) {
-    // first-seen union over the row-major (row, rank) list, lane p = entry p
-    const int n = NB * k;
-    const int e = lane < n ? s.sel[lane / k][lane % k] : -1;
-    int first = lane < n;
-    for (int q = 0; q < n; ++q) {
-      const int eq = __builtin_amdgcn_readlane(e, q);
-      first &= !(q < lane && eq == e);
+    // step 2: exact ranks of the candidates (LDS accesses of one wave
+    // complete in order, so the wave reads back what its lanes wrote)
+    const int nc = s.ncand;
+    if (nc <= 64) {   // lane q holds candidate q; the others come by readlane
+      const bool cq = lane < nc;
+      const int pos = cq ? cand[lane] : 0;
+      const uint64_t kk = cq ? key[pos] : 0;
+      int rank = cq ? cgt[lane] : 0;
+      const int r0 = (pos / Ep) * Ep;
+      for (int q = 0; q < nc; ++q) {
+        const int pq = __builtin_amdgcn_readlane(pos, q);
+        const uint64_t kq = readlane_u64(kk, q);
+        rank += int(pq >= r0 && pq < r0 + Ep && (kq >> 32) == (kk >> 32) &&
+                    (kq > kk || (kq == kk && pq < pos)));
+      }
+      if (cq && rank < k) {
+        s.sel[pos / Ep][rank] = pos - r0;
+        s.selv[pos / Ep][rank] = val[pos];
+      }
+    } else {          // many tied high words: candidates from LDS
+      for (int j = lane; j < nc; j += 64) {
+        const int pos = cand[j];
+        const int r0 = (pos / Ep) * Ep;
+        const uint64_t kk = key[pos];
+        int rank = cgt[j];
+        for (int q = 0; q < nc; ++q) {
+          const int pq = cand[q];
+          const uint64_t kq = key[pq];
+          rank += int(pq >= r0 && pq < r0 + Ep && (kq >> 32) == (kk >> 32) &&
+                      (kq > kk || (kq == kk && pq < pos)));
+        }
+        if (rank < k) {
+          s.sel[pos / Ep][rank] = pos - r0;
+          s.selv[pos / Ep][rank] = val[pos];
+        }
+      }
     }
-    const uint64_t mask = __ballot(first);
-    const int slot = __popcll(mask & ((uint64_t(1) << lane) - 1));
-    const int u = __popcll(mask);
-    if (first) s.uid[slot] = e;
-    if (lane == 0) s.u = u;
     __builtin_amdgcn_wave_barrier();
-    // per-slot descriptor and routing weight of every row; slot u = shared
-    const int j = lane;
-    const int ej = j < u ? s.uid[j] : -1;
-    const uint64_t dj = j < u ? rec_lds[ej] : (j == u ? a.l.shared_rec : 0);
-    s.desc[j] = dj;
-    {
-      const bool ok = j <= u && record_ok(dj, a.l.pool_bytes, a.l.hidden, a.l.inter);
-      const int bt = ok ? bits_of_tag(dj) : 0;
-      const RecordLayout L = record_layout(a.l.hidden, a.l.inter, ok ? bt : 4);
-      const uint8_t *rec = a.l.pool + (dj & ~uint64_t(255));
-      s.dbits[j] = bt;
-      s.dcodes[j] = ok ? rec + L.d_codes : nullptr;
-      s.dsb[j] = ok ? reinterpret_cast<const uint32_t *>(rec + L.d_sb) : nullptr;
+    // lane l < NB k holds entry (row l / k, rank l % k)
+    const int n = NB * k;
+    const bool ent = lane < n;
+    const int lb = ent ? lane / k : 0, lr = lane - lb * k;
+    const int e_l = ent ? s.sel[lb][lr] : 0;
+    const uint64_t d_l = ent ? rec_lds[e_l] : a.l.shared_rec;
+    const double ex = ent ? exp(s.selv[lb][lr] - s.selv[lb][0]) : 0.0;
+    s.exq[lane] = ex;
+    // first-seen union: fq = lowest entry with this lane's expert
+    int fq = lane;
+    for (int q = 0; q < n; ++q) {
+      const int eq = __builtin_amdgcn_readlane(e_l, q);
+      fq = (eq == e_l && q < fq) ? q : fq;
     }
+    const bool first = ent && fq == lane;
+    const uint64_t mask = __ballot(first);
+    const int slot = __popcll(mask & ((uint64_t(1) << fq) - 1));
+    const int u = __popcll(mask);
+    __builtin_amdgcn_wave_barrier();
+    // softmax of each row's k selected logits
+    double sum = 0.0;
+    for (int r = 0; r < k; ++r) sum += s.exq[lb * k + r];
+    const float w_l = ent ? float(ex / sum) : 0.0f;
+    if (ent) s.wsel[lb][lr] = w_l;
+    if (lane == 0) s.u = u;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      float w = 0.0f;
-      for (int r = 0; r < k; ++r) w = (s.sel[b][r] == ej) ? s.wsel[b][r] : w;
-      s.wslot[b][j] = j < u ? w : (j == u ? s.gam[b] : 0.0f);
+    for (int b = 0; b < NB; ++b) s.wslot[b][lane] = lane == u ? s.gam[b] : 0.0f;
+    __builtin_amdgcn_wave_barrier();
+    if (ent) s.wslot[lb][slot] = w_l;
+    // slot records: the first entry of each expert fills its slot, lane 63
+    // (never an entry) the shared expert's slot u
+    if (first || lane == 63) {
+      const int js = first ? slot : u;
+      if (first) s.uid[js] = e_l;
+      s.desc[js] = d_l;
+      const bool ok = record_ok(d_l, a.l.pool_bytes, a.l.hidden, a.l.inter);
+      const int bt = ok ? bits_of_tag(d_l) : 0;
+      const RecordLayout L = record_layout(a.l.hidden, a.l.inter, ok ? bt : 4);
+      const uint8_t *rec = a.l.pool + (d_l & ~uint64_t(255));
+      s.dbits[js] = bt;
+      s.dcodes[js] = ok ? rec + L.d_codes : nullptr;
+      s.dsb[js] = ok ? reinterpret_cast<const uint32_t *>(rec + L.d_sb) : nullptr;
     }
   }
   __syncthreads();
@@ -464,7 +547,7 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
   // build runs between the shared and the routed gate/up units.
   float *xs = reinterpret_cast<float *>(dyn);           // [NB][H]
   float *xsum = xs + NB * H;                            // [NB][H/32]
-  float *keys = xsum + NB * (H / kChunk);               // [NB][E] key, [NB][E] value
+  float *keys = xsum + NB * (H / kChunk);               // routing build scratch
   float *act_lds = xs;                                  // [batch slots][NB][W]
   float *asum_lds = act_lds + kStageCols * kSlotBatch * NB;   // [batch slots][NB][W/32]
 
@@ -472,6 +555,9 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
   const int P = a.per_slice;
 
   if (x < a.n_slices) {
+    const bool route = lr < a.route_blocks;
+    RouterRow<CPL> rrow;
+    if (route) router_prefetch<CPL>(a, lr, rrow);
     for (int e = threadIdx.x; e < a.l.n_experts; e += kThreads) rec_lds[e] = a.l.rec[e];
     for (int i = threadIdx.x * 4; i < NB * H; i += kThreads * 4)
       *reinterpret_cast<float4 *>(xs + i) = *reinterpret_cast<const float4 *>(a.l.x + i);
@@ -487,8 +573,8 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
 
     double *lg = a.l.slice_logits + size_t(x) * kMaxNb * kMaxExperts;
     float *gm = a.l.slice_gamma + x * kMaxNb;
-    if (lr < a.route_blocks) {
-      router_rows<NB>(a, xs, lr, lg, gm);
+    if (route) {
+      router_rows<NB, CPL>(a, xs, lr, rrow, lg, gm);
       block_signal(sw(a, x, kSliceRoute), 1u);
     }
     // the shared expert's gate/up units need no routing
@@ -496,8 +582,7 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
       run_gate_up<NB, CPL>(a, x, a.l.shared_rec, kSharedSlot, i, xs, xsum);
 
     wait_geq(a, sw(a, x, kSliceRoute), uint32_t(a.route_blocks));
-    build_routing<NB>(a, sh, lg, gm, rec_lds, reinterpret_cast<uint64_t *>(keys),
-                      reinterpret_cast<double *>(keys) + NB * kMaxExperts);
+    build_routing<NB>(a, sh, lg, gm, rec_lds, reinterpret_cast<uint8_t *>(keys));
     const int u = sh.u;
     const int n_gu = u * a.ups;
     const int n_total = n_gu + a.tiles;
@@ -528,7 +613,7 @@ size_t dyn_lds_bytes(int nb, int hidden) {
   // x, its per-32 sums and the logit keys; or one batch of staged act chunks
   // and their sums
   const size_t xk = sizeof(float) * (size_t(nb) * hidden + size_t(nb) * (hidden / kChunk)) +
-                    2 * sizeof(double) * size_t(nb) * kMaxExperts;
+                    size_t(nb) * kMaxExperts * (8 + 8 + 4 + 4 + 4);
   const size_t st = sizeof(float) * (size_t(kStageCols) * kSlotBatch * nb + size_t(8) * kSlotBatch * nb);
   return xk > st ? xk : st;
 }
