@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="N",
-                    help="first run N plain 1 GiB device copies (calibrates HBM byte counters)")
+                    help="first run N elementwise passes reading and writing 1 GiB (calibrates HBM byte counters)")
     return ap.parse_args()
 
 
@@ -469,8 +469,10 @@ def bench_decode(moe, torch, syn, name, args, with_cpu):
     log(f"{name}: {statistics.median(us_layer):.2f} us/layer, expert {expert_gbs:.0f} GB/s")
     log(f"{name}: stage pass")
     n_st, layer_us = b.stage_pass(args.stage_steps)
-    k_us = statistics.mean(layer_us)
-    k_bytes = all_b[:n_st].reshape(-1)
+    # the timed region launches exactly one layer kernel per (step, layer) on
+    # one stream, so its event time / launches is the kernel's mean duration
+    k_us = total_ms * 1e3 / (L * args.steps)
+    k_bytes = all_b.reshape(-1)
     k_gbs = float(np.mean(k_bytes)) / (k_us * 1e-6) / 1e9
     out = {
         "config": name,
@@ -486,7 +488,8 @@ def bench_decode(moe, torch, syn, name, args, with_cpu):
         "expert_bytes_per_layer_mean": float(expert_b.mean()),
         "union_mean": float(u.mean()), "union_min": int(u.min()), "union_max": int(u.max()),
         "kernel_us_mean": k_us,
-        "kernel_us_median": statistics.median(layer_us),
+        "eager_launch_us_mean": statistics.mean(layer_us),
+        "eager_launch_us_median": statistics.median(layer_us),
         "stage_steps": n_st,
         "kernel_bytes_per_launch_mean": float(np.mean(k_bytes)),
         "kernel_gbs": k_gbs,
@@ -559,13 +562,14 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     if args.copy_probe:
-        n = 1 << 30
-        src = torch.full((n,), 1, dtype=torch.uint8, device="cuda")
+        # an elementwise kernel (neg) that reads 1 GiB and writes 1 GiB
+        n = 1 << 28
+        src = torch.full((n,), 1.0, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(args.copy_probe):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        log(f"copy probe: {args.copy_probe} copies of {n} bytes")
+        log(f"copy probe: {args.copy_probe} x neg over {4 * n} bytes")
         del src, dst
     main_res = bench_decode(moe, torch, syn, args.config, args, with_cpu=not args.no_cpu)
     extra = {}

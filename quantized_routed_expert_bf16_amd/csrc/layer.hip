@@ -56,7 +56,7 @@ struct LayerArgs {
   int ups;           // gate/up units per slot per slice
   int tiles;         // down tiles (of kRowsPerTile rows)
   int per_slice;     // blocks per slice (gridDim.x / 8)
-  int route_blocks;  // router blocks per slice
+  int route_blocks;  // router blocks in all (block g = lr * n_slices + x)
 };
 
 __device__ inline uint32_t *sw(const LayerArgs &a, int x, int field) {
@@ -113,10 +113,10 @@ struct RouterRow {
 };
 
 template <int CPL>
-__device__ void router_prefetch(const LayerArgs &a, int lr, RouterRow<CPL> &r) {
+__device__ void router_prefetch(const LayerArgs &a, int g, RouterRow<CPL> &r) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int H = a.l.hidden, E = a.l.n_experts;
-  const int e = lr * kWaves + wave;
+  const int e = g * kWaves + wave;
   if (e > E) return;
   const uint16_t *w = e < E ? a.l.router + size_t(e) * H : a.l.gvec;
 #pragma unroll
@@ -125,16 +125,16 @@ __device__ void router_prefetch(const LayerArgs &a, int lr, RouterRow<CPL> &r) {
 }
 
 // Router logits (float64 accumulation of the bf16 weights times x) of rows
-// e = lr * 4 + wave, e += 4 P; row E is the shared expert's gate, stored as
-// its sigmoid.
+// e = 4 g + wave, e += 4 G for router block g of G; row E is the shared
+// expert's gate, stored as its sigmoid.
 template <int NB, int CPL>
-__device__ void router_rows(const LayerArgs &a, const float *xs, int lr, const RouterRow<CPL> &first,
+__device__ void router_rows(const LayerArgs &a, const float *xs, int g, const RouterRow<CPL> &first,
                             double *lg, float *gm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int H = a.l.hidden, E = a.l.n_experts;
-  for (int e = lr * kWaves + wave; e <= E; e += a.per_slice * kWaves) {
+  for (int e = g * kWaves + wave; e <= E; e += a.route_blocks * kWaves) {
     const uint16_t *w = e < E ? a.l.router + size_t(e) * H : a.l.gvec;
-    const bool pre = e == lr * kWaves + wave;
+    const bool pre = e == g * kWaves + wave;
     double acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = 0.0;
@@ -555,9 +555,12 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
   const int P = a.per_slice;
 
   if (x < a.n_slices) {
-    const bool route = lr < a.route_blocks;
+    // router blocks g < G are spread over the slices; R of them are in this one
+    const int g = lr * a.n_slices + x;
+    const bool route = g < a.route_blocks;
+    const int R = x < a.route_blocks ? (a.route_blocks - 1 - x) / a.n_slices + 1 : 0;
     RouterRow<CPL> rrow;
-    if (route) router_prefetch<CPL>(a, lr, rrow);
+    if (route) router_prefetch<CPL>(a, g, rrow);
     for (int e = threadIdx.x; e < a.l.n_experts; e += kThreads) rec_lds[e] = a.l.rec[e];
     for (int i = threadIdx.x * 4; i < NB * H; i += kThreads * 4)
       *reinterpret_cast<float4 *>(xs + i) = *reinterpret_cast<const float4 *>(a.l.x + i);
@@ -571,14 +574,19 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
     }
     __syncthreads();
 
-    double *lg = a.l.slice_logits + size_t(x) * kMaxNb * kMaxExperts;
-    float *gm = a.l.slice_gamma + x * kMaxNb;
+    double *lg = a.l.slice_logits;
+    float *gm = a.l.slice_gamma;
     if (route) {
-      router_rows<NB, CPL>(a, xs, lr, rrow, lg, gm);
-      block_signal(sw(a, x, kSliceRoute), 1u);
+      router_rows<NB, CPL>(a, xs, g, rrow, lg, gm);
+      // every slice counts the router blocks (one counter per slice)
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x < a.n_slices)
+        __hip_atomic_fetch_add(sw(a, threadIdx.x, kSliceRoute), 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
     // the shared expert's gate/up units need no routing
-    for (int i = ((lr - a.route_blocks) % P + P) % P; i < a.ups; i += P)
+    for (int i = ((lr - R) % P + P) % P; i < a.ups; i += P)
       run_gate_up<NB, CPL>(a, x, a.l.shared_rec, kSharedSlot, i, xs, xsum);
 
     wait_geq(a, sw(a, x, kSliceRoute), uint32_t(a.route_blocks));
@@ -586,7 +594,7 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
     const int u = sh.u;
     const int n_gu = u * a.ups;
     const int n_total = n_gu + a.tiles;
-    for (int i = ((lr - a.route_blocks - a.ups) % P + P) % P; i < n_total; i += P) {
+    for (int i = ((lr - R - a.ups) % P + P) % P; i < n_total; i += P) {
       if (i < n_gu) {
         const int slot = i / a.ups;
         run_gate_up<NB, CPL>(a, x, sh.desc[slot], slot, i - slot * a.ups, xs, xsum);
@@ -647,7 +655,7 @@ hipError_t launch_nb(LayerArgs &a, hipStream_t s) {
   }
   const int grid = (per_cu * g_cache.cus) / kSlices * kSlices;
   a.per_slice = grid / kSlices;
-  a.route_blocks = min(a.per_slice, (a.l.n_experts + 1 + kWaves - 1) / kWaves);
+  a.route_blocks = min(a.per_slice * a.n_slices, (a.l.n_experts + 1 + kWaves - 1) / kWaves);
   hipLaunchKernelGGL((layer_kernel<NB, CPL>), dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
