@@ -113,7 +113,7 @@ struct RouterRow {
 };
 
 template <int CPL>
-__device__ void router_prefetch(const LayerArgs &a, int g, RouterRow<CPL> &r) {
+__device__ __forceinline__ void router_prefetch(const LayerArgs &a, int g, RouterRow<CPL> &r) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int H = a.l.hidden, E = a.l.n_experts;
   const int e = g * kWaves + wave;
@@ -128,7 +128,7 @@ __device__ void router_prefetch(const LayerArgs &a, int g, RouterRow<CPL> &r) {
 // e = 4 g + wave, e += 4 G for router block g of G; row E is the shared
 // expert's gate, stored as its sigmoid.
 template <int NB, int CPL>
-__device__ void router_rows(const LayerArgs &a, const float *xs, int g, const RouterRow<CPL> &first,
+__device__ __forceinline__ void router_rows(const LayerArgs &a, const float *xs, int g, const RouterRow<CPL> &first,
                             double *lg, float *gm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int H = a.l.hidden, E = a.l.n_experts;
@@ -178,7 +178,7 @@ __device__ void router_rows(const LayerArgs &a, const float *xs, int g, const Ro
 // selected logits, the first-seen union of the (row, rank) list and the
 // per-slot record pointers used by the expert units.
 template <int NB>
-__device__ void build_routing(const LayerArgs &a, Shared<NB> &s, const double *lg, const float *gm,
+__device__ __forceinline__ void build_routing(const LayerArgs &a, Shared<NB> &s, const double *lg, const float *gm,
                               const uint64_t *rec_lds, uint8_t *kbuf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int E = a.l.n_experts, k = a.l.top_k;
@@ -188,15 +188,28 @@ __device__ void build_routing(const LayerArgs &a, Shared<NB> &s, const double *l
   uint32_t *khi = reinterpret_cast<uint32_t *>(val + NB * kMaxExperts);     // [NB][Ep]
   int *cand = reinterpret_cast<int *>(khi + NB * kMaxExperts);              // candidate position
   int *cgt = cand + NB * kMaxExperts;                                       // its step-1 count
-  for (int p = threadIdx.x; p < NB * Ep; p += kThreads) {
-    const int b = p / Ep, e = p - b * Ep;
-    // + 0.0 folds -0 into +0 so that equal logits tie on the id alone;
-    // padding keys are 0, below every finite logit's key
-    const double v = e < E ? ld_dev(lg + b * kMaxExperts + e) + 0.0 : 0.0;
-    const uint64_t kk = e < E ? order_key(v) : 0;
-    key[p] = kk;
-    val[p] = v;
-    khi[p] = uint32_t(kk >> 32);
+  {   // all of the thread's logit loads in flight at once
+    constexpr int kIt = NB * kMaxExperts / kThreads;
+    double lv[kIt];
+#pragma unroll
+    for (int t = 0; t < kIt; ++t) {   // unconditional loads keep lv in registers
+      const int p = threadIdx.x + t * kThreads, b = p / Ep, e = p - b * Ep;
+      const bool in = p < NB * Ep && e < E;
+      lv[t] = ld_dev(lg + (in ? b * kMaxExperts + e : 0));
+    }
+#pragma unroll
+    for (int t = 0; t < kIt; ++t) {
+      const int p = threadIdx.x + t * kThreads, e = p % Ep;
+      if (p < NB * Ep) {
+        // + 0.0 folds -0 into +0 so that equal logits tie on the id alone;
+        // padding keys are 0, below every finite logit's key
+        const double v = e < E ? lv[t] + 0.0 : 0.0;
+        const uint64_t kk = e < E ? order_key(v) : 0;
+        key[p] = kk;
+        val[p] = v;
+        khi[p] = uint32_t(kk >> 32);
+      }
+    }
   }
   if (threadIdx.x < NB) s.gam[threadIdx.x] = ld_dev(gm + threadIdx.x);
   if (threadIdx.x == 0) s.ncand = 0;
@@ -338,7 +351,7 @@ __device__ void build_routing(const LayerArgs &a, Shared<NB> &s, const double *l
 // 8 row pairs (gate j, up j) of one slot; each wave takes 2, a lane one
 // 32-code chunk of the H inputs (CPL chunks when H > 2048).
 template <int NB, int CPL, int BITS>
-__device__ void gate_up_unit(const LayerArgs &a, const uint8_t *rec, int j0, int act_slot,
+__device__ __forceinline__ void gate_up_unit(const LayerArgs &a, const uint8_t *rec, int j0, int act_slot,
                              const float *xs, const float *xsum) {
   const int lane = threadIdx.x & 63;
   const int H = a.l.hidden, I = a.l.inter;
@@ -413,7 +426,7 @@ __device__ void gate_up_unit(const LayerArgs &a, const uint8_t *rec, int j0, int
 }
 
 template <int NB, int CPL>
-__device__ void run_gate_up(const LayerArgs &a, int x, uint64_t desc, int act_slot, int unit,
+__device__ __forceinline__ void run_gate_up(const LayerArgs &a, int x, uint64_t desc, int act_slot, int unit,
                             const float *xs, const float *xsum) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j0 = x * a.W + unit * kTileRowPairs + wave * kPairsPerWave;
@@ -440,7 +453,7 @@ __device__ void run_gate_up(const LayerArgs &a, int x, uint64_t desc, int act_sl
 // loaded before the wait for the slice's gate/up units, the act chunks with
 // device-coherent loads after it.
 template <int NB>
-__device__ void run_down(const LayerArgs &a, Shared<NB> &sh, int x, int tile, float *act_lds,
+__device__ __forceinline__ void run_down(const LayerArgs &a, Shared<NB> &sh, int x, int tile, float *act_lds,
                          float *asum_lds) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int H = a.l.hidden, I = a.l.inter, W = a.W;
@@ -482,18 +495,30 @@ __device__ void run_down(const LayerArgs &a, Shared<NB> &sh, int x, int tile, fl
     const int nb_slots = min(n_slots - s0, sg * kSlotBatch);
     const int n_f4 = nb_slots * NB * (W / 4);
     __syncthreads();
-    for (int i0 = 0; i0 < n_f4; i0 += kThreads) {
-      const int i = i0 + threadIdx.x;
-      float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (i < n_f4) {
+    constexpr int kStIt = 4;   // loads in flight per thread
+    for (int i0 = 0; i0 < n_f4; i0 += kStIt * kThreads) {
+      float4 f[kStIt];
+#pragma unroll
+      for (int t = 0; t < kStIt; ++t) {   // unconditional loads keep f in registers
+        const int i = min(i0 + t * kThreads + int(threadIdx.x), n_f4 - 1);
         const int q = i % (W / 4), b = (i / (W / 4)) % NB, sl = i / (W / 4) / NB;
         const int slot = s0 + sl;
         const int ps = slot < u ? slot : kSharedSlot;
-        f = ld_dev_f4(a.l.act + (size_t(ps) * kMaxNb + b) * I + x * W + 4 * q);
-        *reinterpret_cast<float4 *>(act_lds + (sl * NB + b) * W + 4 * q) = f;
+        f[t] = ld_dev_f4(a.l.act + (size_t(ps) * kMaxNb + b) * I + x * W + 4 * q);
       }
-      const float cs = group8_sum((f.x + f.y) + (f.z + f.w));   // i = 8 * chunk + (0..7)
-      if (i < n_f4 && (i & 7) == 0) asum_lds[i >> 3] = cs;
+#pragma unroll
+      for (int t = 0; t < kStIt; ++t)
+        if (i0 + t * kThreads + int(threadIdx.x) >= n_f4) f[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int t = 0; t < kStIt; ++t) {
+        const int i = i0 + t * kThreads + threadIdx.x;
+        if (i < n_f4) {
+          const int q = i % (W / 4), b = (i / (W / 4)) % NB, sl = i / (W / 4) / NB;
+          *reinterpret_cast<float4 *>(act_lds + (sl * NB + b) * W + 4 * q) = f[t];
+        }
+        const float cs = group8_sum((f[t].x + f[t].y) + (f[t].z + f[t].w));   // i = 8 chunk + (0..7)
+        if (i < n_f4 && (i & 7) == 0) asum_lds[i >> 3] = cs;
+      }
     }
     __syncthreads();
     // 4. accumulate the lane's slots
@@ -562,8 +587,20 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
     RouterRow<CPL> rrow;
     if (route) router_prefetch<CPL>(a, g, rrow);
     for (int e = threadIdx.x; e < a.l.n_experts; e += kThreads) rec_lds[e] = a.l.rec[e];
-    for (int i = threadIdx.x * 4; i < NB * H; i += kThreads * 4)
-      *reinterpret_cast<float4 *>(xs + i) = *reinterpret_cast<const float4 *>(a.l.x + i);
+    {   // all of the thread's x loads in flight at once (H <= 2048 CPL)
+      constexpr int kXIt = 2 * NB * CPL;
+      float4 xv[kXIt];
+#pragma unroll
+      for (int t = 0; t < kXIt; ++t) {   // unconditional loads keep xv in registers
+        const int i = min((threadIdx.x + t * kThreads) * 4, NB * H - 4);
+        xv[t] = *reinterpret_cast<const float4 *>(a.l.x + i);
+      }
+#pragma unroll
+      for (int t = 0; t < kXIt; ++t) {
+        const int i = (threadIdx.x + t * kThreads) * 4;
+        if (i < NB * H) *reinterpret_cast<float4 *>(xs + i) = xv[t];
+      }
+    }
     __syncthreads();
     for (int i = threadIdx.x; i < NB * (H / kChunk); i += kThreads) {
       const float *p = xs + i * kChunk;
