@@ -41,56 +41,83 @@ constexpr int kSlab = 256;                   // gate/up K slab (4 groups)
 constexpr int kBStride = kSlab + 8;          // halfs per token row in LDS (bank spread)
 
 // ------------------------------------------------------------------ P1
+constexpr int kRouteTok = 4;   // rows per router block
+
+// Block (rb, tg): router rows 4 rb + wave (row E = shared gate) for rows
+// kRouteTok tg .. +kRouteTok, float64 accumulation; then every block takes a
+// share of the x -> f16 hi/lo split and the per-64 group sums.
 __global__ __launch_bounds__(kThreads) void pf_router_kernel(PrefillArgs a, const uint16_t *router,
                                                              const uint16_t *gvec, double *logits,
                                                              float *gamma) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int H = a.hidden, E = a.n_experts, t = a.t;
-  const int e = blockIdx.x * kWaves + wave;
-  if (e <= E) {
+  const int n_rb = (E + 1 + kWaves - 1) / kWaves;
+  const int rb = blockIdx.x % n_rb, r0 = (blockIdx.x / n_rb) * kRouteTok;
+  const int e = rb * kWaves + wave;
+  if (e <= E && r0 < t) {
     const uint16_t *w = e < E ? router + size_t(e) * H : gvec;
-    for (int r0 = 0; r0 < t; r0 += 4) {
-      double acc[4] = {0.0, 0.0, 0.0, 0.0};
-      for (int i0 = lane * 8; i0 < H; i0 += 512) {
-        const uint4 wv = *reinterpret_cast<const uint4 *>(w + i0);
-        const float wf[8] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y),
-                             bf16_lo(wv.z), bf16_hi(wv.z), bf16_lo(wv.w), bf16_hi(wv.w)};
+    double acc[kRouteTok] = {};
+    for (int i0 = lane * 8; i0 < H; i0 += 1024) {
+      uint4 wv[2];
+      float4 xv[2][kRouteTok][2];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          if (r0 + b >= t) break;
-          const float4 x0 = *reinterpret_cast<const float4 *>(a.x + size_t(r0 + b) * H + i0);
-          const float4 x1 = *reinterpret_cast<const float4 *>(a.x + size_t(r0 + b) * H + i0 + 4);
-          const float xf[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      for (int u = 0; u < 2; ++u) {   // two 512-input steps in flight
+        const int i = min(i0 + 512 * u, H - 8);
+        wv[u] = *reinterpret_cast<const uint4 *>(w + i);
+#pragma unroll
+        for (int b = 0; b < kRouteTok; ++b) {
+          const float *xr = a.x + size_t(min(r0 + b, t - 1)) * H + i;
+          xv[u][b][0] = *reinterpret_cast<const float4 *>(xr);
+          xv[u][b][1] = *reinterpret_cast<const float4 *>(xr + 4);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (i0 + 512 * u >= H) break;
+        const float wf[8] = {bf16_lo(wv[u].x), bf16_hi(wv[u].x), bf16_lo(wv[u].y), bf16_hi(wv[u].y),
+                             bf16_lo(wv[u].z), bf16_hi(wv[u].z), bf16_lo(wv[u].w), bf16_hi(wv[u].w)};
+#pragma unroll
+        for (int b = 0; b < kRouteTok; ++b) {
+          const float xf[8] = {xv[u][b][0].x, xv[u][b][0].y, xv[u][b][0].z, xv[u][b][0].w,
+                               xv[u][b][1].x, xv[u][b][1].y, xv[u][b][1].z, xv[u][b][1].w};
 #pragma unroll
           for (int q = 0; q < 8; ++q) acc[b] = fma(double(wf[q]), double(xf[q]), acc[b]);
         }
       }
+    }
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const double v = wave_sum_d(acc[b]);
-        if (lane == 0 && r0 + b < t) {
-          if (e < E) logits[size_t(r0 + b) * E + e] = v;
-          else gamma[r0 + b] = float(1.0 / (1.0 + exp(-v)));
-        }
+    for (int b = 0; b < kRouteTok; ++b) {
+      const double v = wave_sum_d(acc[b]);
+      if (lane == 0 && r0 + b < t) {
+        if (e < E) logits[size_t(r0 + b) * E + e] = v;
+        else gamma[r0 + b] = float(1.0 / (1.0 + exp(-v)));
       }
     }
   }
-  // x -> f16 hi/lo halves and per-64 group sums (one thread per group)
-  const int groups = H / kGroup;
-  for (int i = blockIdx.x * kThreads + threadIdx.x; i < t * groups; i += gridDim.x * kThreads) {
-    const int r = i / groups, g = i - r * groups;
-    const float *src = a.x + size_t(r) * H + g * kGroup;
-    _Float16 *hi = a.xh + size_t(r) * H + g * kGroup;
-    _Float16 *lo = a.xh + size_t(kTok + r) * H + g * kGroup;
+  // x -> f16 hi/lo halves and per-64 group sums: 8 values a thread, the 8
+  // threads of a group add their sums with a DPP reduction
+  for (int i0 = blockIdx.x * kThreads; i0 < t * H / 8; i0 += gridDim.x * kThreads) {
+    const int i = i0 + threadIdx.x;
+    const bool live = i < t * H / 8;
+    const int il = live ? i : 0;
+    const float4 v0 = *reinterpret_cast<const float4 *>(a.x + size_t(il) * 8);
+    const float4 v1 = *reinterpret_cast<const float4 *>(a.x + size_t(il) * 8 + 4);
+    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    _Float16 hi[8], lo[8];
     float sm = 0.0f;
-    for (int q = 0; q < kGroup; ++q) {
-      const float v = src[q];
-      const _Float16 h = _Float16(v);
-      hi[q] = h;
-      lo[q] = _Float16(v - float(h));
-      sm += v;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      hi[q] = _Float16(v[q]);
+      lo[q] = _Float16(v[q] - float(hi[q]));
+      sm += v[q];
     }
-    a.xg[size_t(r) * groups + g] = sm;
+    sm = group8_sum(sm);
+    if (live) {
+      const int r = il / (H / 8), c = (il - r * (H / 8)) * 8;
+      __builtin_memcpy(a.xh + size_t(r) * H + c, hi, 16);
+      __builtin_memcpy(a.xh + size_t(kTok + r) * H + c, lo, 16);
+      if ((il & 7) == 0) a.xg[size_t(r) * (H / kGroup) + c / kGroup] = sm;
+    }
   }
 }
 
@@ -105,6 +132,8 @@ __global__ __launch_bounds__(128) void pf_topk_kernel(PrefillArgs a, const doubl
   __shared__ uint32_t prev;
   __shared__ int all_sel[kTok * kMaxTopK];
   __shared__ int cnt[kMaxExperts + 1];
+  __shared__ uint32_t emask[kMaxExperts];
+  __shared__ int wsum[2];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int E = a.n_experts, k = a.top_k, t = a.t;
   const int r = blockIdx.x;
@@ -141,36 +170,45 @@ __global__ __launch_bounds__(128) void pf_topk_kernel(PrefillArgs a, const doubl
   block_signal(counter, 1u, &prev);
   __syncthreads();
   if (prev != uint32_t(t - 1)) return;
-  // last block: rows grouped by expert, experts ascending, rows ascending
+  // last block: rows grouped by expert, experts ascending, rows ascending.
+  // Each expert gets a mask of the rows that selected it (a row selects an
+  // expert at most once, t <= 32); an entry's place is the expert's start
+  // plus the rows below it in that mask.
   for (int p = threadIdx.x; p < t * k; p += 128) all_sel[p] = int(ld_dev(topk_idx + p));
+  for (int e = threadIdx.x; e < kMaxExperts; e += 128) emask[e] = 0u;
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 128) {
-    int c = 0;
-    for (int p = 0; p < t * k; ++p) c += (all_sel[p] == e);
-    cnt[e] = c;
-  }
+  for (int p = threadIdx.x; p < t * k; p += 128) atomicOr(&emask[all_sel[p]], 1u << (p / k));
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0, used = 0;
-    for (int e = 0; e < E; ++e) {
-      const int c = cnt[e];
-      cnt[e] = run;
-      if (c) a.meta[1 + used++] = e;
-      run += c;
+  // exclusive scan over experts of (rows << 16 | used), two experts a thread
+  {
+    const int e0 = 2 * threadIdx.x, e1 = e0 + 1;
+    const int c0 = e0 < E ? __popc(emask[e0]) : 0, c1 = e1 < E ? __popc(emask[e1]) : 0;
+    const int v0 = (c0 << 16) | int(c0 > 0), v1 = (c1 << 16) | int(c1 > 0);
+    int incl = v0 + v1;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
     }
-    cnt[E] = run;
-    a.meta[0] = used;
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    const int excl = incl - (v0 + v1) + (wave ? wsum[0] : 0);
+    if (e0 < E) { cnt[e0] = excl; }
+    if (e1 < E) { cnt[e1] = excl + v0; }
+    if (threadIdx.x == 0) cnt[E] = wsum[0] + wsum[1];
   }
   __syncthreads();
-  for (int e = threadIdx.x; e <= E; e += 128) expert_ptr[e] = cnt[e];
-  for (int e = threadIdx.x; e < E; e += 128) {
-    int pos = cnt[e];
-    for (int p = 0; p < t * k; ++p)
-      if (all_sel[p] == e) {
-        entry_row[pos] = p / k;
-        entry_rank[pos] = p % k;
-        ++pos;
-      }
+  for (int e = threadIdx.x; e <= E; e += 128) {
+    const int v = cnt[e];
+    expert_ptr[e] = v >> 16;
+    if (e < E && emask[e]) a.meta[1 + (v & 0xffff)] = e;
+  }
+  if (threadIdx.x == 0) a.meta[0] = cnt[E] & 0xffff;
+  for (int p = threadIdx.x; p < t * k; p += 128) {
+    const int e = all_sel[p], r = p / k;
+    const int pos = (cnt[e] >> 16) + __popc(emask[e] & ((1u << r) - 1u));
+    entry_row[pos] = r;
+    entry_rank[pos] = p - r * k;
   }
   if (threadIdx.x == 0) st_dev(counter, 0u);
 }
@@ -559,7 +597,7 @@ hipError_t launch_prefill(const PrefillArgs &a, const uint16_t *router, const ui
     return hipSuccess;
   };
   hipError_t e;
-  const int route_blocks = (a.n_experts + 1 + kWaves - 1) / kWaves;
+  const int route_blocks = (a.n_experts + 1 + kWaves - 1) / kWaves * ((a.t + kRouteTok - 1) / kRouteTok);
   hipLaunchKernelGGL(pf_router_kernel, dim3(route_blocks), dim3(kThreads), 0, s, a, router, gvec,
                      logits, gamma);
   if ((e = hipGetLastError()) != hipSuccess) return e;
