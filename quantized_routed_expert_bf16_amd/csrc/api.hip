@@ -68,11 +68,13 @@ WorkspaceLayout workspace_layout(int hidden, int inter, int n_experts, int top_k
   w.opart = take(size_t(kSlices) * kMaxNb * hidden * sizeof(float));
   w.slice_logits = take(size_t(kSlices) * kMaxNb * kMaxExperts * sizeof(double) +
                         size_t(kSlices) * kMaxNb * sizeof(float));
-  w.pf_xh = take(size_t(2) * MOE_MAX_PREFILL_ROWS * hidden * sizeof(_Float16));
+  w.pf_xf = take(size_t(4) * MOE_MAX_PREFILL_ROWS * hidden * sizeof(_Float16));
   w.pf_xg = take(size_t(MOE_MAX_PREFILL_ROWS) * (hidden / kGroup) * sizeof(float));
-  w.pf_act = take(size_t(pf_rows) * (top_k + 1) * inter * sizeof(float));
+  w.pf_act_rows = pf_rows * (top_k + 1);
+  w.pf_act = take(size_t(2) * w.pf_act_rows * inter * sizeof(_Float16));
+  w.pf_asum = take(size_t(w.pf_act_rows) * (inter / 32) * sizeof(float));
   w.pf_y = take(size_t(pf_rows) * (top_k + 1) * hidden * sizeof(float));
-  w.pf_meta = take(size_t(1 + kMaxExperts) * sizeof(int32_t));
+  w.pf_meta = take(size_t(1 + 2 * (2 * kMaxExperts + 2)) * sizeof(int32_t));
   w.total = pos;
   return w;
 }
@@ -299,9 +301,11 @@ int moe_prefill_forward(const float *x, int32_t t, const moe_router *router, moe
   pa.n_experts = d.n_experts;
   pa.top_k = d.top_k;
   pa.t = t;
-  pa.xh = reinterpret_cast<_Float16 *>(ws + L.pf_xh);
+  pa.xf = reinterpret_cast<_Float16 *>(ws + L.pf_xf);
   pa.xg = reinterpret_cast<float *>(ws + L.pf_xg);
-  pa.act = reinterpret_cast<float *>(ws + L.pf_act);
+  pa.act = reinterpret_cast<_Float16 *>(ws + L.pf_act);
+  pa.asum = reinterpret_cast<float *>(ws + L.pf_asum);
+  pa.act_rows = L.pf_act_rows;
   pa.y = reinterpret_cast<float *>(ws + L.pf_y);
   pa.meta = reinterpret_cast<int32_t *>(ws + L.pf_meta);
   pa.status = reinterpret_cast<uint32_t *>(ws + L.counters) + kSyncStatus;

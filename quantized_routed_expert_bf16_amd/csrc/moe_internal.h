@@ -98,11 +98,13 @@ struct WorkspaceLayout {
   size_t act;          // decode: [64][4][I] f32
   size_t opart;        // decode: [8][4][H] f32 per-slice partial outputs
   size_t slice_logits; // decode: [8][4][256] f64, [8][4] f32 gamma after it
-  size_t pf_xh;        // prefill: [2][32][H] f16 hi/lo split of x
+  size_t pf_xf;        // prefill: [2 orders][hi, lo][32][H] f16 MFMA-ordered x
   size_t pf_xg;        // prefill: [32][H/64] f32 group sums of x
-  size_t pf_act;       // prefill: [t*k + t][I] f32 act per entry
+  size_t pf_act;       // prefill: [hi, lo][t*k + t][I] f16 MFMA-ordered act per entry
+  int pf_act_rows;     // entries pf_act holds
+  size_t pf_asum;      // prefill: [t*k + t][I/32] f32 sums of 32-column act blocks
   size_t pf_y;         // prefill: [t][k+1][H] f32 weighted outputs per (row, rank)
-  size_t pf_meta;      // prefill: [1 + 256] i32 used experts
+  size_t pf_meta;      // prefill: sub-job count, then (expert, first row) pairs
   size_t total;
 };
 
@@ -141,11 +143,13 @@ struct PrefillArgs {
   float *topk_w;               // [t][k]
   const float *gamma;          // [t]
   int hidden, inter, n_experts, top_k, t;
-  _Float16 *xh;                // [2][32][H]: f16 hi rows, then lo rows
+  _Float16 *xf;                // [2 orders][hi, lo][32][H]: x split in f16 halves, MFMA order
   float *xg;                   // [32][H/64] group sums of x
-  float *act;                  // [t*k + t][I] silu(g)*u per entry (shared entries last)
+  _Float16 *act;               // [hi, lo][act_rows][I]: silu(g)*u per entry, same split and order
+  float *asum;                 // [act_rows][I/32] sums of act over 32-column blocks
+  int act_rows;                // entries the act buffer holds (shared entries last)
   float *y;                    // [t][k+1][H] weighted output per (row, rank); rank k = shared
-  int32_t *meta;               // [1 + E]: used-expert count, then their ids ascending
+  int32_t *meta;               // sub-job count, then (expert or -1, first row) per sub-job
   uint32_t *status;
   float *out;                  // [t][H]
 };

@@ -37,8 +37,28 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTok = MOE_MAX_PREFILL_ROWS;   // 32 token slots per expert
-constexpr int kSlab = 256;                   // gate/up K slab (4 groups)
-constexpr int kBStride = kSlab + 8;          // halfs per token row in LDS (bank spread)
+
+// MFMA operand order.  A lane feeds 16 codes of a 64-code group to two
+// 16x16x32 steps; position p = 8 s + j of its 16 (step s, half j) holds code
+// frag_code(order, p) of them.  Order 0 (4-bit records: nibble pairs q and
+// q + 4 of a word) and order 1 (2/3-bit records: fields q and q + 8) follow
+// from how the codes unpack into f16 pairs; x and act are stored in the same
+// order so that a lane's B fragment is 16 contiguous bytes.
+__host__ __device__ constexpr int frag_code(int order, int p) {
+  return order == 0 ? 8 * (p >> 3) + ((p & 7) >> 1) + 4 * (p & 1)
+                    : 4 * (p >> 3) + ((p & 7) >> 1) + 8 * (p & 1);
+}
+__host__ __device__ constexpr int frag_pos(int order, int c) {   // inverse of frag_code
+  return order == 0 ? 8 * (c >> 3) + 2 * ((c & 7) & 3) + ((c & 7) >> 2)
+                    : 8 * ((c & 7) >> 2) + 2 * (c & 3) + (c >> 3);
+}
+constexpr bool frag_maps_inverse() {
+  for (int o = 0; o < 2; ++o)
+    for (int p = 0; p < 16; ++p)
+      if (frag_pos(o, frag_code(o, p)) != p) return false;
+  return true;
+}
+static_assert(frag_maps_inverse(), "frag_pos must invert frag_code");
 
 // ------------------------------------------------------------------ P1
 constexpr int kRouteTok = 4;   // rows per router block
@@ -94,29 +114,40 @@ __global__ __launch_bounds__(kThreads) void pf_router_kernel(PrefillArgs a, cons
       }
     }
   }
-  // x -> f16 hi/lo halves and per-64 group sums: 8 values a thread, the 8
-  // threads of a group add their sums with a DPP reduction
-  for (int i0 = blockIdx.x * kThreads; i0 < t * H / 8; i0 += gridDim.x * kThreads) {
-    const int i = i0 + threadIdx.x;
-    const bool live = i < t * H / 8;
-    const int il = live ? i : 0;
-    const float4 v0 = *reinterpret_cast<const float4 *>(a.x + size_t(il) * 8);
-    const float4 v1 = *reinterpret_cast<const float4 *>(a.x + size_t(il) * 8 + 4);
-    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    _Float16 hi[8], lo[8];
-    float sm = 0.0f;
+  // x -> f16 hi/lo halves in both MFMA code orders: one 16-code block a
+  // thread (4-bit order at xf[0], 2/3-bit order at xf[1])
+  for (int i0 = blockIdx.x * kThreads; i0 < t * H / 16; i0 += gridDim.x * kThreads) {
+    // (t H / 16 is a multiple of 16, so whole 64-lane groups stay together)
+    const int i = min(i0 + int(threadIdx.x), t * H / 16 - 1);
+    const bool live = i0 + int(threadIdx.x) < t * H / 16;
+    const int r = i / (H / 16), c = (i - r * (H / 16)) * 16;
+    float v[16];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      hi[q] = _Float16(v[q]);
-      lo[q] = _Float16(v[q] - float(hi[q]));
-      sm += v[q];
+    for (int q = 0; q < 4; ++q) {
+      const float4 f = *reinterpret_cast<const float4 *>(a.x + size_t(r) * H + c + 4 * q);
+      v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
     }
-    sm = group8_sum(sm);
-    if (live) {
-      const int r = il / (H / 8), c = (il - r * (H / 8)) * 8;
-      __builtin_memcpy(a.xh + size_t(r) * H + c, hi, 16);
-      __builtin_memcpy(a.xh + size_t(kTok + r) * H + c, lo, 16);
-      if ((il & 7) == 0) a.xg[size_t(r) * (H / kGroup) + c / kGroup] = sm;
+    {   // per-64 group sums of x: the 4 threads of a group combine over DPP
+      float sm = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) sm += v[q];
+      sm += dpp_f<kDppXor1>(sm);
+      sm += dpp_f<kDppXor2>(sm);
+      if (live && (i & 3) == 0) a.xg[size_t(r) * (H / kGroup) + c / kGroup] = sm;
+    }
+#pragma unroll
+    for (int fam = 0; fam < 2; ++fam) {
+      _Float16 hi[16], lo[16];
+#pragma unroll
+      for (int p = 0; p < 16; ++p) {
+        const float x = v[frag_code(fam, p)];
+        hi[p] = _Float16(x);
+        lo[p] = _Float16(x - float(hi[p]));
+      }
+      if (live) {
+        __builtin_memcpy(a.xf + (size_t(2 * fam) * kTok + r) * H + c, hi, 32);
+        __builtin_memcpy(a.xf + (size_t(2 * fam + 1) * kTok + r) * H + c, lo, 32);
+      }
     }
   }
 }
@@ -179,11 +210,14 @@ __global__ __launch_bounds__(128) void pf_topk_kernel(PrefillArgs a, const doubl
   __syncthreads();
   for (int p = threadIdx.x; p < t * k; p += 128) atomicOr(&emask[all_sel[p]], 1u << (p / k));
   __syncthreads();
-  // exclusive scan over experts of (rows << 16 | used), two experts a thread
+  // exclusive scan over experts of (rows << 20 | big << 10 | used), two
+  // experts a thread: `used` numbers the experts in use, `big` those with
+  // more than 16 rows (they run as two sub-jobs of at most 16 rows)
   {
     const int e0 = 2 * threadIdx.x, e1 = e0 + 1;
     const int c0 = e0 < E ? __popc(emask[e0]) : 0, c1 = e1 < E ? __popc(emask[e1]) : 0;
-    const int v0 = (c0 << 16) | int(c0 > 0), v1 = (c1 << 16) | int(c1 > 0);
+    const int v0 = (c0 << 20) | (int(c0 > 16) << 10) | int(c0 > 0);
+    const int v1 = (c1 << 20) | (int(c1 > 16) << 10) | int(c1 > 0);
     int incl = v0 + v1;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -198,15 +232,33 @@ __global__ __launch_bounds__(128) void pf_topk_kernel(PrefillArgs a, const doubl
     if (threadIdx.x == 0) cnt[E] = wsum[0] + wsum[1];
   }
   __syncthreads();
+  // sub-jobs (expert, first row): experts ascending, then the shared expert
   for (int e = threadIdx.x; e <= E; e += 128) {
     const int v = cnt[e];
-    expert_ptr[e] = v >> 16;
-    if (e < E && emask[e]) a.meta[1 + (v & 0xffff)] = e;
+    expert_ptr[e] = v >> 20;
+    if (e < E && emask[e]) {
+      const int sj = ((v >> 10) & 1023) + (v & 1023);
+      a.meta[1 + 2 * sj] = e;
+      a.meta[2 + 2 * sj] = 0;
+      if (__popc(emask[e]) > 16) {
+        a.meta[3 + 2 * sj] = e;
+        a.meta[4 + 2 * sj] = 16;
+      }
+    }
   }
-  if (threadIdx.x == 0) a.meta[0] = cnt[E] & 0xffff;
+  if (threadIdx.x == 0) {
+    const int v = cnt[E], n_sub = ((v >> 10) & 1023) + (v & 1023);
+    a.meta[1 + 2 * n_sub] = -1;
+    a.meta[2 + 2 * n_sub] = 0;
+    if (t > 16) {
+      a.meta[3 + 2 * n_sub] = -1;
+      a.meta[4 + 2 * n_sub] = 16;
+    }
+    a.meta[0] = n_sub + (t > 16 ? 2 : 1);
+  }
   for (int p = threadIdx.x; p < t * k; p += 128) {
     const int e = all_sel[p], r = p / k;
-    const int pos = (cnt[e] >> 16) + __popc(emask[e] & ((1u << r) - 1u));
+    const int pos = (cnt[e] >> 20) + __popc(emask[e] & ((1u << r) - 1u));
     entry_row[pos] = r;
     entry_rank[pos] = p - r * k;
   }
@@ -255,9 +307,6 @@ __device__ inline void codes_to_a(const uint32_t (&w)[3], half8 (&A)[2], int hsh
   }
 }
 
-__device__ inline int code_offset(int bits, int s, int j) {
-  return bits == 4 ? 8 * s + j / 2 + 4 * (j % 2) : 4 * s + j / 2 + 8 * (j % 2);
-}
 
 // 16 codes of one lane for one 64-code group: codes [16g, 16g+16) of the
 // group starting at code index `c0` of a packed row (`row` points at the row,
@@ -278,298 +327,351 @@ __device__ inline void load16(const uint8_t *row, int row_codes, int c0, uint32_
   }
 }
 
+// A sub-job: at most 16 rows of one expert (or of the shared expert).
 struct Job {
   int e;        // expert id, or -1 for the shared expert
   int base;     // first entry index of its rows
-  int m;        // rows
+  int m;        // rows (1..16)
   uint64_t desc;
 };
 
-__device__ inline bool job_of(const PrefillArgs &a, int ui, Job &j) {
-  const int n_used = a.meta[0];
-  if (ui < n_used) {
-    j.e = a.meta[1 + ui];
-    j.base = a.expert_ptr[j.e];
-    j.m = a.expert_ptr[j.e + 1] - j.base;
+__device__ inline bool job_of(const PrefillArgs &a, int sj, Job &j) {
+  if (sj >= a.meta[0]) return false;
+  j.e = a.meta[1 + 2 * sj];
+  const int off = a.meta[2 + 2 * sj];
+  if (j.e >= 0) {
+    const int b0 = a.expert_ptr[j.e];
+    j.base = b0 + off;
+    j.m = min(16, a.expert_ptr[j.e + 1] - b0 - off);
     j.desc = a.rec[j.e];
-    return true;
-  }
-  if (ui == n_used) {
-    j.e = -1;
-    j.base = a.t * a.top_k;
-    j.m = a.t;
+  } else {
+    j.base = a.t * a.top_k + off;
+    j.m = min(16, a.t - off);
     j.desc = a.shared_rec;
-    return true;
   }
-  return false;
+  return true;
 }
 
+// token row of a sub-job's n-th entry
 __device__ inline int entry_token_row(const PrefillArgs &a, const Job &j, int n) {
-  return j.e < 0 ? n : a.entry_row[j.base + n];
+  return j.e < 0 ? j.base - a.t * a.top_k + n : a.entry_row[j.base + n];
+}
+
+// ------------------------------------------------------- P3 / P4 tiles
+// One work item: 64 output rows (16 per wave) of one sub-job (m <= 16 token
+// rows, one 16-column MFMA tile), over K = n_groups 64-code groups.  The
+// B rows (f16 hi and lo halves, already in MFMA order), the tile's (scale,
+// bias) words and the B rows' group sums go straight from global memory into
+// LDS (global_load_lds: lane i's 16 or 4 bytes land at base + 16 i or 4 i),
+// CG groups at a time: all of K for up to 8 rows, half of it for up to 16
+// (H = 2048); the lane's codes for 32 groups load into registers at once.
+// Few, large rounds: each round costs one memory latency.  Token slots past
+// the job's rows hold stale LDS contents: an MFMA output column depends on
+// its own B column only, and those columns are never stored.
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
+
+constexpr int kCodeGroups = 32;                 // groups of codes held in registers
+constexpr int kBufHalfs = 16 * (16 * kGroup + 8) > 8 * (32 * kGroup + 8) ? 16 * (16 * kGroup + 8)
+                                                                         : 8 * (32 * kGroup + 8);
+struct TileBuf {
+  __attribute__((aligned(16))) _Float16 bh[kBufHalfs];
+  __attribute__((aligned(16))) _Float16 bl[kBufHalfs];
+  __attribute__((aligned(16))) uint32_t sb[32 * 64];   // [group][64 rows] (scale, bias) words
+  float xs[16 * 16 * 2];                               // [token][group][part] B group sums
+};
+
+// Where a work item's operands live.
+struct TileSrc {
+  __amdgpu_buffer_rsrc_t codes;   // A: the record's code section
+  bool group_major;       // D layout [group][row][64 codes] (else [row][K codes])
+  int row_bytes;          // bytes per packed row (row-major layout)
+  int rows_total;         // rows of the matrix (group-major layout)
+  const uint32_t *sb;     // (scale, bias) words
+  bool sb_group_major;    // [group][rows] (else [row][groups])
+  int sb_stride;          // groups per row, or rows per group
+  const _Float16 *bh, *bl;   // B rows (row stride = K halfs)
+  const float *xsum;      // B group sums, `parts` per group (row stride = parts n_groups)
+  int parts;
+  int K;                  // codes per row = 64 n_groups
+  int r0;                 // first of the tile's 64 rows
+  int m;                  // token rows of the job (<= 16)
+  const int *brow;        // LDS: B row of each token slot
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0,
+                                           int(bytes < 0x7fffffffu ? bytes : 0x7fffffffu), 0x00020000);
+}
+
+// 16 codes of a lane for one group: the same words load16 reads, by offset.
+template <int BITS>
+__device__ __forceinline__ void load_codes(const TileSrc &src, int row, int grp, int g, uint32_t (&w)[3]) {
+  uint32_t off, hi_off = 0;
+  if (src.group_major) {
+    const uint32_t base = (uint32_t(grp) * src.rows_total + row) * (kGroup * BITS / 8);
+    off = base + 16 * g * BITS / 8;
+    if constexpr (BITS == 3) { off = base + 16 * g / 4; hi_off = base + kGroup / 4 + (16 * g / 32) * 4; }
+  } else {
+    const uint32_t base = uint32_t(row) * src.row_bytes, c0 = grp * kGroup + 16 * g;
+    off = base + c0 * (BITS == 4 ? 4 : 2) / 8;
+    if constexpr (BITS == 3) hi_off = base + src.K / 4 + (c0 / 32) * 4;
+  }
+  w[2] = 0;
+  if constexpr (BITS == 4) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(src.codes, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1];
+  } else {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(src.codes, off, 0, 0);
+    w[1] = BITS == 3 ? __builtin_amdgcn_raw_buffer_load_b32(src.codes, hi_off, 0, 0) : 0u;
+  }
+}
+
+// LDS loads of groups [g0, g0 + gq) into `buf`; wave w takes every fourth.
+template <int CG>
+__device__ __forceinline__ void chunk_dma(const TileSrc &src, TileBuf &buf, int g0, int gq, int n_groups) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kRow = CG * kGroup + 8;            // B row stride in LDS (halfs)
+  constexpr int kSegs = CG * kGroup / 512;         // 1 KB segments per B row
+  // B rows: one load per (token row, hi/lo, segment)
+  for (int q = wave; q < 2 * kSegs * src.m; q += kWaves) {
+    const int n = q / (2 * kSegs), hl = (q / kSegs) & 1, seg = q % kSegs;
+    const int k0 = seg * 512 + lane * 8;
+    const _Float16 *row = (hl ? src.bl : src.bh) + size_t(src.brow[n]) * src.K + g0 * kGroup;
+    _Float16 *dst = (hl ? buf.bl : buf.bh) + n * kRow + seg * 512;
+    if (k0 < gq * kGroup)
+      __builtin_amdgcn_global_load_lds((gvoid *)(row + k0), (lvoid *)dst, 16, 0, 0);
+  }
+  // (scale, bias) words: one load per group, lane = tile row
+  for (int Q = wave; Q < gq; Q += kWaves) {
+    const int row = src.r0 + lane, grp = g0 + Q;
+    const uint32_t *p = src.sb_group_major ? src.sb + size_t(grp) * src.sb_stride + row
+                                           : src.sb + size_t(row) * src.sb_stride + grp;
+    __builtin_amdgcn_global_load_lds((gvoid *)p, (lvoid *)(buf.sb + Q * 64), 4, 0, 0);
+  }
+  // group sums: entry i = (token n, group Q, part h)
+  const int ents = src.m * CG * src.parts;
+  for (int q = wave; q * 64 < ents; q += kWaves) {
+    const int i = q * 64 + lane, n = i / (CG * src.parts), Q = (i / src.parts) % CG, h = i % src.parts;
+    if (i < ents && Q < gq) {
+      const float *p = src.xsum + (size_t(src.brow[n]) * n_groups + g0 + Q) * src.parts + h;
+      __builtin_amdgcn_global_load_lds((gvoid *)p, (lvoid *)(buf.xs + q * 64), 4, 0, 0);
+    }
+  }
+}
+
+template <int BITS, int CG>
+__device__ __forceinline__ void chunk_mma(const TileSrc &src, const TileBuf &buf, const uint32_t (&w)[kCodeGroups][3],
+                                          int q0, int gq, floatx4 &acc) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // token slot of the lane's B column; with 32-group rounds only 8 rows are
+  // staged, so slots 8..15 (past m) read rows 0..7 (their columns are unused)
+  const int g = lane >> 4, n = CG == 32 ? (lane & 7) : (lane & 15);
+  constexpr int kRow = CG * kGroup + 8;
+#pragma unroll
+  for (int Q = 0; Q < CG; ++Q) {
+    if (Q < gq) {
+      half8 A[2];
+      codes_to_a<BITS>(w[q0 + Q], A, g & 1);
+      const uint4 sq = *static_cast<const uint4 *>(__builtin_assume_aligned(buf.sb + Q * 64 + wave * 16 + 4 * g, 16));
+      const uint32_t sw4[4] = {sq.x, sq.y, sq.z, sq.w};
+      floatx4 cgv = {0, 0, 0, 0};
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int at = n * kRow + Q * kGroup + 16 * g + 8 * st;
+        const half8 Bh = *static_cast<const half8 *>(__builtin_assume_aligned(buf.bh + at, 16));
+        const half8 Bl = *static_cast<const half8 *>(__builtin_assume_aligned(buf.bl + at, 16));
+        cgv = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[st], Bh, cgv, 0, 0, 0);
+        cgv = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[st], Bl, cgv, 0, 0, 0);
+      }
+      const float *xp = buf.xs + (n * CG + Q) * src.parts;
+      const float xs = src.parts == 2 ? xp[0] + xp[1] : xp[0];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = fmaf(sb_scale(sw4[q]), cgv[q], fmaf(sb_bias(sw4[q]), xs, acc[q]));
+    }
+  }
+}
+
+template <int BITS, int CG>
+__device__ __forceinline__ void mfma_tile(const TileSrc &src, TileBuf &buf, floatx4 &acc) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int arow = src.r0 + wave * 16 + (lane & 15), g = lane >> 4;
+  const int n_groups = src.K / kGroup;
+  acc = floatx4{0, 0, 0, 0};
+  for (int g0 = 0; g0 < n_groups; g0 += kCodeGroups) {
+    uint32_t w[kCodeGroups][3];
+#pragma unroll
+    for (int Q = 0; Q < kCodeGroups; ++Q) load_codes<BITS>(src, arow, min(g0 + Q, n_groups - 1), g, w[Q]);
+#pragma unroll
+    for (int cs = 0; cs < kCodeGroups / CG; ++cs) {
+      const int cb = g0 + cs * CG;
+      if (cb < n_groups) {
+        const int gq = min(CG, n_groups - cb);
+        __syncthreads();                 // the buffer's previous reads are done
+        chunk_dma<CG>(src, buf, cb, gq, n_groups);
+        __builtin_amdgcn_s_waitcnt(0);   // this round's LDS loads and the codes have landed
+        __syncthreads();                 // ... for every wave
+        chunk_mma<BITS, CG>(src, buf, w, cs * CG, gq, acc);
+      }
+    }
+  }
+  __syncthreads();   // the buffer is free for the next work item
+}
+
+template <int BITS>
+__device__ __forceinline__ void mfma_tile_any(const TileSrc &src, TileBuf &buf, floatx4 &acc) {
+  if (src.m > 8) mfma_tile<BITS, 16>(src, buf, acc);   // (rounds of 32 groups hold 8 rows)
+  else mfma_tile<BITS, 32>(src, buf, acc);
+}
+
+__device__ __forceinline__ void set_brows(const PrefillArgs &a, const Job &j, int *brow, bool act_rows) {
+  for (int n = threadIdx.x; n < j.m; n += kThreads)
+    brow[n] = act_rows ? j.base + n : entry_token_row(a, j, n);
 }
 
 // ------------------------------------------------------------------ P3
-template <int BITS>
-__device__ void gate_up_tile(const PrefillArgs &a, const Job &j, int tile, _Float16 *bh, _Float16 *bl,
-                             float *xg_lds, uint32_t *sb_lds) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int H = a.hidden, I = a.inter, groups = H / kGroup;
-  const RecordLayout L = record_layout(H, I, BITS);
-  const uint8_t *rec = a.pool + (j.desc & ~uint64_t(255));
-  const int R0 = tile * 64 + wave * 16;            // first gate/up row of this wave
-  const int arow = R0 + (lane & 15), g = lane >> 4;
-  const uint8_t *codes = rec + L.gu_codes + size_t(arow) * L.gu_row_bytes;
-  const uint32_t *sb = reinterpret_cast<const uint32_t *>(rec + L.gu_sb);
-  const int nt = (j.m + 15) / 16;
-  floatx4 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-
-  for (int slab = 0; slab < H / kSlab; ++slab) {
-    __syncthreads();
-    // stage x (hi, lo) of the tokens for this slab in MFMA B order, and the
-    // group sums of x; padding tokens are zero
-    for (int it = threadIdx.x; it < kTok * 16; it += kThreads) {
-      const int n = it >> 4, Q = (it >> 2) & 3, gg = it & 3;
-      const int k0 = slab * kSlab + 64 * Q + 16 * gg;
-      _Float16 vh[16], vl[16];
-      if (n < j.m) {
-        const int row = entry_token_row(a, j, n);
-        const uint4 *ph = reinterpret_cast<const uint4 *>(a.xh + size_t(row) * H + k0);
-        const uint4 *pl = reinterpret_cast<const uint4 *>(a.xh + size_t(kTok + row) * H + k0);
-        const uint4 h0 = ph[0], h1 = ph[1], l0 = pl[0], l1 = pl[1];
-        __builtin_memcpy(vh, &h0, 16); __builtin_memcpy(vh + 8, &h1, 16);
-        __builtin_memcpy(vl, &l0, 16); __builtin_memcpy(vl + 8, &l1, 16);
-      } else {
-        for (int q = 0; q < 16; ++q) vh[q] = vl[q] = _Float16(0.0f);
-      }
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        _Float16 oh[8], ol[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int o = code_offset(BITS, s, jj);
-          oh[jj] = vh[o];
-          ol[jj] = vl[o];
-        }
-        const int at = n * kBStride + ((Q * 4 + gg) * 2 + s) * 8;
-        __builtin_memcpy(bh + at, oh, 16);
-        __builtin_memcpy(bl + at, ol, 16);
-      }
-    }
-    for (int it = threadIdx.x; it < kTok * 4; it += kThreads) {
-      const int n = it >> 2, Q = it & 3;
-      xg_lds[it] = n < j.m ? a.xg[size_t(entry_token_row(a, j, n)) * groups + slab * 4 + Q] : 0.0f;
-    }
-    // (scale, bias) of the 16 rows x 4 groups of each wave, for the C layout
-    {
-      const int rr = R0 + (lane >> 2), Q = lane & 3;
-      sb_lds[wave * 64 + lane] = sb[size_t(rr) * groups + slab * 4 + Q];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int Q = 0; Q < 4; ++Q) {
-      uint32_t w[3];
-      load16<BITS>(codes, H, slab * kSlab + 64 * Q + 16 * g, w);
-      half8 A[2];
-      codes_to_a<BITS>(w, A, (g & 1));
-      float sc[4], bi[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t v = sb_lds[wave * 64 + (4 * g + q) * 4 + Q];
-        sc[q] = sb_scale(v);
-        bi[q] = sb_bias(v);
-      }
-      for (int tt = 0; tt < nt; ++tt) {
-        floatx4 cg = {0, 0, 0, 0};
-        const int n = tt * 16 + (lane & 15);
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int at = n * kBStride + ((Q * 4 + g) * 2 + s) * 8;
-          const half8 Bh = *reinterpret_cast<const half8 *>(bh + at);
-          const half8 Bl = *reinterpret_cast<const half8 *>(bl + at);
-          cg = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[s], Bh, cg, 0, 0, 0);
-          cg = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[s], Bl, cg, 0, 0, 0);
-        }
-        const float xs = xg_lds[n * 4 + Q];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[tt][q] += fmaf(sc[q], cg[q], bi[q] * xs);
-      }
-    }
-  }
-  // rows 4g+q of the tile: (gate, up) pairs (q = 0,1) and (q = 2,3)
-  for (int tt = 0; tt < nt; ++tt) {
-    const int n = tt * 16 + (lane & 15);
-    if (n >= j.m) continue;
-    const int p0 = (R0 + 4 * g) / 2;
-    float *dst = a.act + size_t(j.base + n) * I;
-    dst[p0] = silu_mul(acc[tt][0], acc[tt][1]);
-    dst[p0 + 1] = silu_mul(acc[tt][2], acc[tt][3]);
-  }
-}
-
+// gate/up: work item (job, 64 interleaved gate/up rows); act = silu(g) * u
+// of the tile's 32 columns, stored as f16 hi/lo halves in the MFMA order of
+// the job's record, plus the sum of the 32 values for the down pass's bias
+// term.
 __global__ __launch_bounds__(kThreads) void pf_gate_up_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 bh[kTok * kBStride];
-  __shared__ __attribute__((aligned(16))) _Float16 bl[kTok * kBStride];
-  __shared__ float xg_lds[kTok * 4];
-  __shared__ uint32_t sb_lds[kWaves * 64];
-  const int tiles = 2 * a.inter / 64;
-  const int n_jobs = a.meta[0] + 1;
-  for (int w = blockIdx.x; w < n_jobs * tiles; w += gridDim.x) {
-    Job j;
-    if (!job_of(a, w / tiles, j)) break;
-    if (!record_ok(j.desc, a.pool_bytes, a.hidden, a.inter)) {
-      if (threadIdx.x == 0) __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      // zero this tile's act values so the down pass stays finite
-      const int tile = w % tiles;
-      for (int i = threadIdx.x; i < j.m * 32; i += kThreads)
-        a.act[size_t(j.base + i / 32) * a.inter + tile * 32 + i % 32] = 0.0f;
-      continue;
-    }
-    switch (bits_of_tag(j.desc)) {
-      case 4: gate_up_tile<4>(a, j, w % tiles, bh, bl, xg_lds, sb_lds); break;
-      case 3: gate_up_tile<3>(a, j, w % tiles, bh, bl, xg_lds, sb_lds); break;
-      default: gate_up_tile<2>(a, j, w % tiles, bh, bl, xg_lds, sb_lds); break;
-    }
-  }
-}
-
-// ------------------------------------------------------------------ P4
-constexpr int kActStride = 512 + 8;   // halfs per token row of one 512-wide K pass
-
-template <int BITS>
-__device__ void down_tile(const PrefillArgs &a, const Job &j, int tile, _Float16 *ah, _Float16 *al,
-                          float *as_lds, float *sb_lds) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int H = a.hidden, I = a.inter, gpr = I / kGroup;
-  const RecordLayout L = record_layout(H, I, BITS);
-  const uint8_t *rec = a.pool + (j.desc & ~uint64_t(255));
-  const uint32_t *sb = reinterpret_cast<const uint32_t *>(rec + L.d_sb);
-  const int R0 = tile * 64 + wave * 16;            // first output row of this wave
-  const int arow = R0 + (lane & 15), g = lane >> 4;
-  const int nt = (j.m + 15) / 16;
-  const int gb = kGroup * BITS / 8;                // bytes of one row's group
-  floatx4 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-
-  for (int k0 = 0; k0 < I; k0 += 512) {            // K passes of up to 8 groups
-    const int gq = min(8, (I - k0) / kGroup);
-    __syncthreads();
-    for (int it = threadIdx.x; it < kTok * gq * 4; it += kThreads) {
-      const int n = it / (gq * 4), Q = (it >> 2) % gq, gg = it & 3;
-      float v[16];
-      if (n < j.m) {
-        const float *src = a.act + size_t(j.base + n) * I + k0 + 64 * Q + 16 * gg;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 f = *reinterpret_cast<const float4 *>(src + 4 * q);
-          v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
-        }
-      } else {
-        for (int q = 0; q < 16; ++q) v[q] = 0.0f;
-      }
-      float sm = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) sm += v[q];
-      as_lds[it] = sm;                                      // [n][Q][gg] partial sums
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        _Float16 oh[8], ol[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const float x = v[code_offset(BITS, s, jj)];
-          oh[jj] = _Float16(x);
-          ol[jj] = _Float16(x - float(oh[jj]));
-        }
-        const int at = n * kActStride + ((Q * 4 + gg) * 2 + s) * 8;
-        __builtin_memcpy(ah + at, oh, 16);
-        __builtin_memcpy(al + at, ol, 16);
-      }
-    }
-    for (int it = threadIdx.x; it < 64 * gq; it += kThreads) {   // 64 rows x gq groups
-      const int wv = it / (16 * gq), rr = (it / gq) % 16, Q = it % gq;
-      const int row = tile * 64 + wv * 16 + rr;
-      sb_lds[(wv * 16 + rr) * 8 + Q] = __uint_as_float(sb[size_t(k0 / kGroup + Q) * H + row]);
-    }
-    __syncthreads();
-    for (int Q = 0; Q < gq; ++Q) {
-      const int grp = k0 / kGroup + Q;
-      uint32_t w[3];
-      const uint8_t *grow = rec + L.d_codes + (size_t(grp) * H + arow) * gb;
-      load16<BITS>(grow, kGroup, 16 * g, w);
-      half8 A[2];
-      codes_to_a<BITS>(w, A, (g & 1));
-      float sc[4], bi[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t v = __float_as_uint(sb_lds[(wave * 16 + 4 * g + q) * 8 + Q]);
-        sc[q] = sb_scale(v);
-        bi[q] = sb_bias(v);
-      }
-      for (int tt = 0; tt < nt; ++tt) {
-        floatx4 cg = {0, 0, 0, 0};
-        const int n = tt * 16 + (lane & 15);
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int at = n * kActStride + ((Q * 4 + g) * 2 + s) * 8;
-          const half8 Bh = *reinterpret_cast<const half8 *>(ah + at);
-          const half8 Bl = *reinterpret_cast<const half8 *>(al + at);
-          cg = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[s], Bh, cg, 0, 0, 0);
-          cg = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[s], Bl, cg, 0, 0, 0);
-        }
-        const float* asn = as_lds + (n * gq + Q) * 4;
-        const float xs = (asn[0] + asn[1]) + (asn[2] + asn[3]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[tt][q] += fmaf(sc[q], cg[q], bi[q] * xs);
-      }
-    }
-  }
-  (void)gpr;
-  // routing-weighted output rows of every entry, one (row, rank) slot each
-  for (int tt = 0; tt < nt; ++tt) {
-    const int n = tt * 16 + (lane & 15);
-    if (n >= j.m) continue;
-    const int p = j.base + n;
-    int row, rank;
-    float wgt;
-    if (j.e < 0) {
-      row = n;
-      rank = a.top_k;
-      wgt = a.gamma[n];
-    } else {
-      row = a.entry_row[p];
-      rank = a.entry_rank[p];
-      wgt = a.topk_w[row * a.top_k + rank];
-    }
-    float *dst = a.y + (size_t(row) * (a.top_k + 1) + rank) * H + R0 + 4 * g;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) dst[q] = wgt * acc[tt][q];
-  }
-}
-
-__global__ __launch_bounds__(kThreads) void pf_down_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 ah[kTok * kActStride];
-  __shared__ __attribute__((aligned(16))) _Float16 al[kTok * kActStride];
-  __shared__ float as_lds[kTok * 8 * 4];
-  __shared__ float sb_lds[64 * 8];
-  const int tiles = a.hidden / 64;
-  const int n_jobs = a.meta[0] + 1;
+  __shared__ TileBuf buf;
+  __shared__ int brow[16];
+  __shared__ float red[kWaves][16];
+  const int H = a.hidden, I = a.inter;
+  const int tiles = 2 * I / 64;
+  const int n_jobs = a.meta[0];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, nl = lane & 15;
   for (int w = blockIdx.x; w < n_jobs * tiles; w += gridDim.x) {
     Job j;
     if (!job_of(a, w / tiles, j)) break;
     const int tile = w % tiles;
-    if (!record_ok(j.desc, a.pool_bytes, a.hidden, a.inter)) {
-      if (threadIdx.x == 0) __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      for (int i = threadIdx.x; i < j.m * 64; i += kThreads) {
-        const int n = i / 64, h = tile * 64 + i % 64;
-        const int row = j.e < 0 ? n : a.entry_row[j.base + n];
-        const int rank = j.e < 0 ? a.top_k : a.entry_rank[j.base + n];
-        a.y[(size_t(row) * (a.top_k + 1) + rank) * a.hidden + h] = 0.0f;
+    const bool ok = record_ok(j.desc, a.pool_bytes, H, I);
+    const int bits = ok ? bits_of_tag(j.desc) : 4, order = bits == 4 ? 0 : 1;
+    floatx4 acc = {0, 0, 0, 0};
+    if (ok) {
+      const RecordLayout R = record_layout(H, I, bits);
+      const uint8_t *rec = a.pool + (j.desc & ~uint64_t(255));
+      set_brows(a, j, brow, false);
+      __syncthreads();
+      TileSrc src;
+      src.codes = rsrc(rec + R.gu_codes, R.gu_sb - R.gu_codes);
+      src.group_major = false;
+      src.row_bytes = R.gu_row_bytes;
+      src.rows_total = 2 * I;
+      src.sb = reinterpret_cast<const uint32_t *>(rec + R.gu_sb);
+      src.sb_group_major = false;
+      src.sb_stride = H / kGroup;
+      src.bh = a.xf + size_t(2 * order) * kTok * H;
+      src.bl = a.xf + size_t(2 * order + 1) * kTok * H;
+      src.xsum = a.xg;
+      src.parts = 1;
+      src.K = H;
+      src.r0 = tile * 64;
+      src.m = j.m;
+      src.brow = brow;
+      switch (bits) {
+        case 4: mfma_tile_any<4>(src, buf, acc); break;
+        case 3: mfma_tile_any<3>(src, buf, acc); break;
+        default: mfma_tile_any<2>(src, buf, acc); break;
       }
-      continue;
+    } else if (threadIdx.x == 0) {
+      __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    switch (bits_of_tag(j.desc)) {
-      case 4: down_tile<4>(a, j, tile, ah, al, as_lds, sb_lds); break;
-      case 3: down_tile<3>(a, j, tile, ah, al, as_lds, sb_lds); break;
-      default: down_tile<2>(a, j, tile, ah, al, as_lds, sb_lds); break;
+    // lane rows 4g + q: (gate, up) pairs q = (0, 1) and (2, 3); a bad record
+    // leaves zeros so that the down pass stays finite
+    const int p0 = (tile * 64 + wave * 16 + 4 * g) / 2;
+    float v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) v[h] = ok ? silu_mul(acc[2 * h], acc[2 * h + 1]) : 0.0f;
+    if (nl < j.m) {
+      _Float16 *dh = a.act + size_t(j.base + nl) * I;
+      _Float16 *dl = a.act + (size_t(a.act_rows) + j.base + nl) * I;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int col = p0 + h;
+        const int at = (col & ~15) + frag_pos(order, col & 15);
+        const _Float16 hv = _Float16(v[h]);
+        dh[at] = hv;
+        dl[at] = _Float16(v[h] - float(hv));
+      }
     }
+    // the tile's 32 columns of token nl: 2 per lane, 4 lanes (g) per wave
+    float sm = v[0] + v[1];
+    sm += __shfl_xor(sm, 16);
+    sm += __shfl_xor(sm, 32);
+    if (g == 0) red[wave][nl] = sm;
+    __syncthreads();
+    if (int(threadIdx.x) < j.m)
+      a.asum[size_t(j.base + threadIdx.x) * (I / 32) + tile] =
+          (red[0][threadIdx.x] + red[1][threadIdx.x]) + (red[2][threadIdx.x] + red[3][threadIdx.x]);
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ P4
+// down: work item (job, 64 output rows); writes the routing-weighted rows of
+// every (row, rank) entry of the job.
+__global__ __launch_bounds__(kThreads) void pf_down_kernel(PrefillArgs a) {
+  __shared__ TileBuf buf;
+  __shared__ int brow[16];
+  const int H = a.hidden, I = a.inter;
+  const int tiles = H / 64;
+  const int n_jobs = a.meta[0];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, nl = lane & 15;
+  for (int w = blockIdx.x; w < n_jobs * tiles; w += gridDim.x) {
+    Job j;
+    if (!job_of(a, w / tiles, j)) break;
+    const int tile = w % tiles;
+    const bool ok = record_ok(j.desc, a.pool_bytes, H, I);
+    floatx4 acc = {0, 0, 0, 0};
+    if (ok) {
+      const int bits = bits_of_tag(j.desc);
+      const RecordLayout R = record_layout(H, I, bits);
+      const uint8_t *rec = a.pool + (j.desc & ~uint64_t(255));
+      set_brows(a, j, brow, true);
+      __syncthreads();
+      TileSrc src;
+      src.codes = rsrc(rec + R.d_codes, R.d_sb - R.d_codes);
+      src.group_major = true;
+      src.row_bytes = R.d_row_bytes;
+      src.rows_total = H;
+      src.sb = reinterpret_cast<const uint32_t *>(rec + R.d_sb);
+      src.sb_group_major = true;
+      src.sb_stride = H;
+      src.bh = a.act;
+      src.bl = a.act + size_t(a.act_rows) * I;
+      src.xsum = a.asum;
+      src.parts = 2;
+      src.K = I;
+      src.r0 = tile * 64;
+      src.m = j.m;
+      src.brow = brow;
+      switch (bits) {
+        case 4: mfma_tile_any<4>(src, buf, acc); break;
+        case 3: mfma_tile_any<3>(src, buf, acc); break;
+        default: mfma_tile_any<2>(src, buf, acc); break;
+      }
+    } else if (threadIdx.x == 0) {
+      __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (nl < j.m) {
+      int row, rank;
+      float wgt;
+      if (j.e < 0) {
+        row = entry_token_row(a, j, nl);
+        rank = a.top_k;
+        wgt = a.gamma[row];
+      } else {
+        row = a.entry_row[j.base + nl];
+        rank = a.entry_rank[j.base + nl];
+        wgt = a.topk_w[row * a.top_k + rank];
+      }
+      float *dst = a.y + (size_t(row) * (a.top_k + 1) + rank) * H + tile * 64 + wave * 16 + 4 * g;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[q] = ok ? wgt * acc[q] : 0.0f;
+    }
+    __syncthreads();   // brow is rewritten by the next work item
   }
 }
 
