@@ -363,22 +363,23 @@ __device__ inline int entry_token_row(const PrefillArgs &a, const Job &j, int n)
 // B rows (f16 hi and lo halves, already in MFMA order), the tile's (scale,
 // bias) words and the B rows' group sums go straight from global memory into
 // LDS (global_load_lds: lane i's 16 or 4 bytes land at base + 16 i or 4 i),
-// CG groups at a time: all of K for up to 8 rows, half of it for up to 16
-// (H = 2048); the lane's codes for 32 groups load into registers at once.
-// Few, large rounds: each round costs one memory latency.  Token slots past
+// CG groups at a time (16 for up to 8 rows, 8 for up to 16); the lane's
+// codes for 32 groups load into registers at once.  The buffer is small
+// enough for three blocks per CU, whose load and compute phases interleave.  Token slots past
 // the job's rows hold stale LDS contents: an MFMA output column depends on
 // its own B column only, and those columns are never stored.
 typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
 
 constexpr int kCodeGroups = 32;                 // groups of codes held in registers
-constexpr int kBufHalfs = 16 * (16 * kGroup + 8) > 8 * (32 * kGroup + 8) ? 16 * (16 * kGroup + 8)
-                                                                         : 8 * (32 * kGroup + 8);
+// one round: 16 rows of 8 groups, or 8 rows of 16 groups
+constexpr int kBufHalfs = 16 * (8 * kGroup + 8) > 8 * (16 * kGroup + 8) ? 16 * (8 * kGroup + 8)
+                                                                       : 8 * (16 * kGroup + 8);
 struct TileBuf {
   __attribute__((aligned(16))) _Float16 bh[kBufHalfs];
   __attribute__((aligned(16))) _Float16 bl[kBufHalfs];
-  __attribute__((aligned(16))) uint32_t sb[32 * 64];   // [group][64 rows] (scale, bias) words
-  float xs[16 * 16 * 2];                               // [token][group][part] B group sums
+  __attribute__((aligned(16))) uint32_t sb[16 * 64];   // [group][64 rows] (scale, bias) words
+  float xs[8 * 16 * 2];                                // [token][group][part] B group sums
 };
 
 // Where a work item's operands live.
@@ -464,9 +465,9 @@ template <int BITS, int CG>
 __device__ __forceinline__ void chunk_mma(const TileSrc &src, const TileBuf &buf, const uint32_t (&w)[kCodeGroups][3],
                                           int q0, int gq, floatx4 &acc) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // token slot of the lane's B column; with 32-group rounds only 8 rows are
+  // token slot of the lane's B column; with 16-group rounds only 8 rows are
   // staged, so slots 8..15 (past m) read rows 0..7 (their columns are unused)
-  const int g = lane >> 4, n = CG == 32 ? (lane & 7) : (lane & 15);
+  const int g = lane >> 4, n = CG == 16 ? (lane & 7) : (lane & 15);
   constexpr int kRow = CG * kGroup + 8;
 #pragma unroll
   for (int Q = 0; Q < CG; ++Q) {
@@ -520,8 +521,8 @@ __device__ __forceinline__ void mfma_tile(const TileSrc &src, TileBuf &buf, floa
 
 template <int BITS>
 __device__ __forceinline__ void mfma_tile_any(const TileSrc &src, TileBuf &buf, floatx4 &acc) {
-  if (src.m > 8) mfma_tile<BITS, 16>(src, buf, acc);   // (rounds of 32 groups hold 8 rows)
-  else mfma_tile<BITS, 32>(src, buf, acc);
+  if (src.m > 8) mfma_tile<BITS, 8>(src, buf, acc);   // (rounds of 16 groups hold 8 rows)
+  else mfma_tile<BITS, 16>(src, buf, acc);
 }
 
 __device__ __forceinline__ void set_brows(const PrefillArgs &a, const Job &j, int *brow, bool act_rows) {
