@@ -19,6 +19,8 @@ oracle on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
+import pathlib
 import json
 import os
 import statistics
@@ -30,6 +32,36 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD public figure
 METRIC = "µs per MoE layer and expert-weight GB/s (% HBM peak) at nb=1,4"
+
+
+ROOT = pathlib.Path(__file__).resolve().parent
+TRAFFIC_FILE = ROOT / "profiles" / "layer_kernel_decode_nb1_traffic.md"
+LAYER_SOURCES = ("layer.hip", "device_common.h", "moe_internal.h")
+
+
+def layer_source_hash():
+    h = hashlib.sha256()
+    for f in LAYER_SOURCES:
+        h.update((ROOT / "quantized_routed_expert_bf16_amd" / "csrc" / f).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config):
+    """HBM bytes per layer-kernel launch from the committed counter summary,
+    or None when it was taken on other kernel sources or another workload."""
+    if config != "decode_nb1" or not TRAFFIC_FILE.exists():
+        return None
+    fields = {}
+    for line in TRAFFIC_FILE.read_text().splitlines():
+        if ":" in line and not line.startswith((" ", "#", "`")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != layer_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def log(*a):
@@ -600,7 +632,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "layer_kernel (the fused decode layer)",
                      "achieved": round(main_res["kernel_gbs"], 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(main_res["kernel_gbs"] / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(args.config),
                      "bytes_per_launch": round(main_res["kernel_bytes_per_launch_mean"]),
                      "us_per_launch": round(main_res["kernel_us_mean"], 3)},
         "cpu_baseline": main_res.get("cpu"),

@@ -160,24 +160,27 @@ int moe_layer_forward(const float *x, int32_t nb, const moe_router *router,
                       const moe_shared *shared, float *out, void *stream);
 
 /* One prefill chunk of t rows (1..32): route every row, group rows by expert,
- * run each used expert on its rows with MFMA tiles (8/16/32-row tiles), the
- * shared expert on all rows, and combine per row in a fixed order.
+ * run each used expert on its rows with MFMA tiles (sub-jobs of at most 16
+ * rows), the shared expert on all rows, and combine per row in a fixed order.
  * Struct Gpu prepare_expert_jobs / pf_experts.  out: device f32 [t][H]. */
 int moe_prefill_forward(const float *x, int32_t t, const moe_router *router,
                         moe_prefill_plan *plan, const moe_pool *pool,
                         const moe_shared *shared, float *out, void *stream);
 
 /* Status word kept in the workspace: bit 0 set when a kernel met a record
- * descriptor outside the pool or with tag 3 (that expert was skipped).
- * Synchronises `stream`, reads the word and clears it; <0 on error. */
+ * descriptor outside the pool or with tag 3 (that expert was skipped; its
+ * contribution is zero); bit 2 set when the decode kernel's bounded wait for
+ * another block ran out (its output is then not valid).  Synchronises
+ * `stream`, reads the word and clears it; <0 on error. */
 int moe_workspace_status(void *ws, size_t ws_bytes, void *stream);
 
 /* Profiling hook (the analog of per-phase GPU timestamps): for the calling
- * thread, moe_layer_forward records events[i] (hipEvent_t, created by the
- * caller) on its stream right after its i-th kernel -- 0: route, 1: gate/up,
- * 2: down/combine -- and moe_prefill_forward after its own kernels in order.
- * Entries may be NULL; n = 0 turns the hook off.  No work is skipped.  At
- * most 8 events. */
+ * thread, each call records events[i] (hipEvent_t, created by the caller) on
+ * its stream.  moe_layer_forward runs one fused kernel and records events[0]
+ * right after it.  moe_prefill_forward records events[0] after routing, top-k
+ * and the expert grouping, events[1] after gate/up, events[2] after down and
+ * events[3] after the per-row combine.  Entries may be NULL; n = 0 turns the
+ * hook off.  No work is skipped.  At most 8 events. */
 int moe_set_stage_events(void *const *events, int32_t n);
 
 /* Text of the last non-zero return on the calling thread ("" if none). */
