@@ -102,6 +102,7 @@ struct Shared {
   float gam[NB];
   int u;
   uint32_t prev;
+  uint32_t ep;        // this call's epoch
 };
 
 // ----------------------------------------------------------------- route
@@ -539,20 +540,44 @@ __device__ __forceinline__ void run_down(const LayerArgs &a, Shared<NB> &sh, int
         acc[b] = fmaf(sh.wslot[b][slot], fmaf(sc, P[b], bi * asum_lds[(sl * NB + b) * cpr + c]), acc[b]);
     }
   }
-  // sum the row's 8 lanes (chunks x slot groups) and publish the slice partial
+  // sum the row's 8 lanes (chunks x slot groups) and publish the slice
+  // partial, tagged with this call's epoch: no wait and no counter, the
+  // combining block checks every partial's tag
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = group8_sum(acc[b]);
-  if (idx == 0)
+  if ((threadIdx.x & 7) == 0)
 #pragma unroll
-    for (int b = 0; b < NB; ++b) st_dev(a.l.opart + (size_t(x) * kMaxNb + b) * H + row, acc[b]);
+    for (int b = 0; b < NB; ++b)
+      st_dev(a.l.opart + (size_t(x) * kMaxNb + b) * H + row,
+             (uint64_t(sh.ep) << 32) | __float_as_uint(acc[b]));
 
-  block_signal(a.l.sync + kSyncTile + tile, 1u, &sh.prev);
-  __syncthreads();
-  if (sh.prev == uint32_t(a.n_slices - 1)) {   // last slice of this tile: combine
+  if (tile % a.n_slices == x) {   // this slice's block combines the tile's rows in slice order
     for (int i = threadIdx.x; i < kRowsPerTile * NB; i += kThreads) {
       const int b = i / kRowsPerTile, r = tile * kRowsPerTile + i % kRowsPerTile;
+      uint64_t w[kSlices];
+#pragma unroll
+      for (int q = 0; q < kSlices; ++q)
+        w[q] = q < a.n_slices ? ld_dev(a.l.opart + (size_t(q) * kMaxNb + b) * H + r) : 0;
+      for (uint32_t it = 1;; ++it) {   // re-read the partials not yet of this call (bounded)
+        bool all = true;
+#pragma unroll
+        for (int q = 0; q < kSlices; ++q) all &= q >= a.n_slices || uint32_t(w[q] >> 32) == sh.ep;
+        if (all) break;
+        if ((it & 63) == 0 && (ld_dev(a.l.sync + kSyncAbort) || it > kSpinLimit)) {
+          st_dev(a.l.sync + kSyncAbort, 1u);
+          set_status(a, 4u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+        for (int q = 0; q < kSlices; ++q)
+          if (q < a.n_slices && uint32_t(w[q] >> 32) != sh.ep)
+            w[q] = ld_dev(a.l.opart + (size_t(q) * kMaxNb + b) * H + r);
+      }
       float v = 0.0f;
-      for (int q = 0; q < a.n_slices; ++q) v += ld_dev(a.l.opart + (size_t(q) * kMaxNb + b) * H + r);
+#pragma unroll
+      for (int q = 0; q < kSlices; ++q)
+        if (q < a.n_slices) v += __uint_as_float(uint32_t(w[q]));
       a.l.out[size_t(b) * H + r] = v;
     }
   }
@@ -578,6 +603,12 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
 
   const int x = blockIdx.x % kSlices, lr = blockIdx.x / kSlices;
   const int P = a.per_slice;
+  // this call's epoch (tags the slice partials); never 0, the workspace's
+  // initial tag
+  if (threadIdx.x == 0) {
+    const uint32_t e = ld_dev(a.l.sync + kSyncEpoch) + 1u;
+    sh.ep = e ? e : 1u;
+  }
 
   if (x < a.n_slices) {
     // router blocks g < G are spread over the slices; R of them are in this one
@@ -647,9 +678,9 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
   if (sh.prev == uint32_t(P - 1)) {
     block_signal(a.l.sync + kSyncExit, 1u, &sh.prev);
     __syncthreads();
-    if (sh.prev == uint32_t(kSlices - 1)) {
+    if (sh.prev == uint32_t(kSlices - 1)) {   // every block has read the epoch: publish it
       for (int i = threadIdx.x; i < kSyncWords; i += kThreads)
-        if (i != kSyncStatus) st_dev(a.l.sync + i, 0u);
+        if (i != kSyncStatus) st_dev(a.l.sync + i, i == kSyncEpoch ? sh.ep : 0u);
     }
   }
 }

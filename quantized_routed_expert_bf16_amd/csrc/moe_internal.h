@@ -87,7 +87,7 @@ struct LayerLaunch {
   float *out;                // [nb][H]
   uint32_t *sync;            // 256 counter words (workspace head)
   float *act;                // [64][4][I]
-  float *opart;              // [8][4][H]  per-slice partial outputs
+  uint64_t *opart;           // [8][4][H]  per-slice partial outputs: epoch << 32 | f32 bits
   double *slice_logits;      // [8][4][256] per-slice router logits
   float *slice_gamma;        // [8][4]
 };
@@ -96,7 +96,7 @@ struct LayerLaunch {
 struct WorkspaceLayout {
   size_t counters;     // kSyncWords u32 counter / status words
   size_t act;          // decode: [64][4][I] f32
-  size_t opart;        // decode: [8][4][H] f32 per-slice partial outputs
+  size_t opart;        // decode: [8][4][H] per-slice partial outputs (epoch-tagged f32)
   size_t slice_logits; // decode: [8][4][256] f64, [8][4] f32 gamma after it
   size_t pf_xf;        // prefill: [2 orders][hi, lo][32][H] f16 MFMA-ordered x
   size_t pf_xg;        // prefill: [32][H/64] f32 group sums of x
@@ -122,6 +122,7 @@ constexpr int kSyncRoute = 512;             // standalone route kernel: blocks a
 constexpr int kSyncStatus = 520;            // bit 0: bad descriptor skipped; bit 2: a wait ran out
 constexpr int kSyncExit = 528;              // slices whose blocks all left
 constexpr int kSyncAbort = 576;             // set when a wait ran out: all waits fall through
+constexpr int kSyncEpoch = 608;             // decode: number of the last finished call (tags data)
 constexpr int kSyncTile = 640;              // 256 words: slices done per down row tile
 constexpr int kMaxDownTiles = 256;
 
