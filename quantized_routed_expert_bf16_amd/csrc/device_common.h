@@ -123,6 +123,97 @@ __device__ inline void chunk_dot(const uint32_t (&w)[4], const XSrc &X, float (&
   }
 }
 
+// chunk_dot for R rows that share the operand: each float4 of x is read once
+// and applied to all R rows right away, so no row keeps x in registers.
+template <int BITS, int NB, int R, typename XSrc>
+__device__ inline void chunk_dot_rows(const uint32_t (&w)[R][4], const XSrc &X, float (&P)[R][NB]) {
+  if constexpr (BITS == 4) {
+    float lo[R][NB], hi[R][NB];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) lo[r][b] = hi[r][b] = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      float cl[R][4], ch[R][4];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t l = w[r][m] & 0x0f0f0f0fu, h = w[r][m] & 0xf0f0f0f0u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) { cl[r][k] = byte_f(l, k); ch[r][k] = byte_f(h, k); }
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float4 x0 = X(b, 2 * m), x1 = X(b, 2 * m + 1);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          lo[r][b] = fmaf(cl[r][0], x0.x, lo[r][b]);
+          hi[r][b] = fmaf(ch[r][0], x0.y, hi[r][b]);
+          lo[r][b] = fmaf(cl[r][1], x0.z, lo[r][b]);
+          hi[r][b] = fmaf(ch[r][1], x0.w, hi[r][b]);
+          lo[r][b] = fmaf(cl[r][2], x1.x, lo[r][b]);
+          hi[r][b] = fmaf(ch[r][2], x1.y, hi[r][b]);
+          lo[r][b] = fmaf(cl[r][3], x1.z, lo[r][b]);
+          hi[r][b] = fmaf(ch[r][3], x1.w, hi[r][b]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) P[r][b] = fmaf(hi[r][b], 0.0625f, lo[r][b]);
+  } else {
+    float acc[R][4][NB];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[r][p][b] = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      uint32_t lm[R][4], hm[R][4];   // field p of every byte (low plane, high bit)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          lm[r][p] = w[r][m] & (0x03030303u << (2 * p));
+          hm[r][p] = BITS == 3 ? w[r][2] & (0x01010101u << (4 * m + p)) : 0u;
+        }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float c[R][4];   // [row][p]: codes 16m+4k+p
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            c[r][p] = byte_f(lm[r][p], k);
+            if constexpr (BITS == 3) {
+              const float hs = (m == 0) ? float(4 << p) : float(4 << p) / 16.0f;
+              c[r][p] = fmaf(byte_f(hm[r][p], k), hs, c[r][p]);
+            }
+          }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const float4 xv = X(b, 4 * m + k);
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            acc[r][0][b] = fmaf(c[r][0], xv.x, acc[r][0][b]);
+            acc[r][1][b] = fmaf(c[r][1], xv.y, acc[r][1][b]);
+            acc[r][2][b] = fmaf(c[r][2], xv.z, acc[r][2][b]);
+            acc[r][3][b] = fmaf(c[r][3], xv.w, acc[r][3][b]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        P[r][b] = acc[r][0][b] + 0.25f * acc[r][1][b] + 0.0625f * acc[r][2][b] + 0.015625f * acc[r][3][b];
+  }
+}
+
 // Operand sources for chunk_dot.
 template <int NB>
 struct RegX {   // x[b][0..31] in registers

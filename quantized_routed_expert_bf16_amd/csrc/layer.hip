@@ -108,9 +108,18 @@ struct Shared {
 // ----------------------------------------------------------------- route
 // A wave's first router row (or the shared-expert gate vector, row E), loaded
 // into registers before the block stages x so that both loads overlap.
+// x in LDS, chunk-major: the 4-float group q (0..7) of 32-input chunk c of
+// row b is float4 number (8 b + q) n_chunks + c, so a wave whose lanes read
+// chunks lane + 64 t touches consecutive float4s (no bank conflicts).
+struct ChunkX {
+  const float4 *p;
+  int nch, c;
+  __device__ float4 operator()(int b, int q) const { return p[(b * 8 + q) * nch + c]; }
+};
+
 template <int CPL>
 struct RouterRow {
-  uint4 w[4 * CPL];   // lane's 8 bf16 at inputs 8 lane + 512 t
+  uint4 w[4 * CPL];   // lane's 32 bf16 of chunk lane + 64 (t / 4), 8 per uint4
 };
 
 template <int CPL>
@@ -121,18 +130,20 @@ __device__ __forceinline__ void router_prefetch(const LayerArgs &a, int g, Route
   if (e > E) return;
   const uint16_t *w = e < E ? a.l.router + size_t(e) * H : a.l.gvec;
 #pragma unroll
-  for (int t = 0; t < 4 * CPL; ++t)
-    if (lane * 8 + 512 * t < H) r.w[t] = *reinterpret_cast<const uint4 *>(w + lane * 8 + 512 * t);
+  for (int t = 0; t < 4 * CPL; ++t) {
+    const int c = lane + 64 * (t / 4);
+    if (c < H / kChunk) r.w[t] = *reinterpret_cast<const uint4 *>(w + c * kChunk + 8 * (t % 4));
+  }
 }
 
 // Router logits (float64 accumulation of the bf16 weights times x) of rows
 // e = 4 g + wave, e += 4 G for router block g of G; row E is the shared
-// expert's gate, stored as its sigmoid.
+// expert's gate, stored as its sigmoid.  Lane l takes chunks l + 64 t.
 template <int NB, int CPL>
 __device__ __forceinline__ void router_rows(const LayerArgs &a, const float *xs, int g, const RouterRow<CPL> &first,
                             double *lg, float *gm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int H = a.l.hidden, E = a.l.n_experts;
+  const int H = a.l.hidden, E = a.l.n_experts, nch = H / kChunk;
   for (int e = g * kWaves + wave; e <= E; e += a.route_blocks * kWaves) {
     const uint16_t *w = e < E ? a.l.router + size_t(e) * H : a.l.gvec;
     const bool pre = e == g * kWaves + wave;
@@ -141,15 +152,15 @@ __device__ __forceinline__ void router_rows(const LayerArgs &a, const float *xs,
     for (int b = 0; b < NB; ++b) acc[b] = 0.0;
 #pragma unroll
     for (int t = 0; t < 4 * CPL; ++t) {
-      const int i0 = lane * 8 + 512 * t;
-      if (i0 >= H) break;
-      const uint4 wv = pre ? first.w[t] : *reinterpret_cast<const uint4 *>(w + i0);
+      const int c = lane + 64 * (t / 4), j = t % 4;
+      if (c >= nch) break;
+      const uint4 wv = pre ? first.w[t] : *reinterpret_cast<const uint4 *>(w + c * kChunk + 8 * j);
       const float wf[8] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y),
                            bf16_lo(wv.z), bf16_hi(wv.z), bf16_lo(wv.w), bf16_hi(wv.w)};
+      const ChunkX X{reinterpret_cast<const float4 *>(xs), nch, c};
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const float4 x0 = *reinterpret_cast<const float4 *>(xs + b * H + i0);
-        const float4 x1 = *reinterpret_cast<const float4 *>(xs + b * H + i0 + 4);
+        const float4 x0 = X(b, 2 * j), x1 = X(b, 2 * j + 1);
         const float xf[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[b] = fma(double(wf[q]), double(xf[q]), acc[b]);
@@ -389,30 +400,47 @@ __device__ __forceinline__ void gate_up_unit(const LayerArgs &a, const uint8_t *
       for (int b = 0; b < NB; ++b) v[p][h][b] = 0.0f;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    const int chunk = lane + 64 * c;
-    const bool live = chunk < n_chunks;
-    float xr[NB][kChunk];
+    const int chunk = min(lane + 64 * c, n_chunks - 1);
+    const bool live = lane + 64 * c < n_chunks;
+    const ChunkX X{reinterpret_cast<const float4 *>(xs), n_chunks, chunk};
     float xsm[NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
+    for (int b = 0; b < NB; ++b) xsm[b] = live ? xsum[b * n_chunks + chunk] : 0.0f;
+    if constexpr (NB <= 2) {   // x of the chunk in registers, shared by the four rows
+      float xr[NB][kChunk];
 #pragma unroll
-      for (int q = 0; q < kChunk / 4; ++q) {
-        float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (live) f = *reinterpret_cast<const float4 *>(xs + b * H + chunk * kChunk + 4 * q);
-        xr[b][4 * q] = f.x; xr[b][4 * q + 1] = f.y; xr[b][4 * q + 2] = f.z; xr[b][4 * q + 3] = f.w;
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int q = 0; q < kChunk / 4; ++q) {
+          const float4 f = X(b, q);
+          xr[b][4 * q] = f.x; xr[b][4 * q + 1] = f.y; xr[b][4 * q + 2] = f.z; xr[b][4 * q + 3] = f.w;
+        }
+#pragma unroll
+      for (int p = 0; p < kPairsPerWave; ++p)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float P[NB];
+          chunk_dot<BITS, NB>(w[p][h][c], RegX<NB>{xr}, P);
+          const float sc = sb_scale(s[p][h][c]), bi = sb_bias(s[p][h][c]);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) v[p][h][b] += fmaf(sc, P[b], bi * xsm[b]);
+        }
+    } else {   // more rows: each x float4 from LDS feeds the four rows at once
+      constexpr int R = 2 * kPairsPerWave;
+      uint32_t wr[R][4];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wr[r][q] = w[r / 2][r % 2][c][q];
+      float P[R][NB];
+      chunk_dot_rows<BITS, NB, R>(wr, X, P);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float sc = sb_scale(s[r / 2][r % 2][c]), bi = sb_bias(s[r / 2][r % 2][c]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) v[r / 2][r % 2][b] += fmaf(sc, P[r][b], bi * xsm[b]);
       }
-      xsm[b] = live ? xsum[b * (H / kChunk) + chunk] : 0.0f;
     }
-#pragma unroll
-    for (int p = 0; p < kPairsPerWave; ++p)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float P[NB];
-        chunk_dot<BITS, NB>(w[p][h][c], RegX<NB>{xr}, P);
-        const float sc = sb_scale(s[p][h][c]), bi = sb_bias(s[p][h][c]);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) v[p][h][b] += fmaf(sc, P[b], bi * xsm[b]);
-      }
   }
 #pragma unroll
   for (int p = 0; p < kPairsPerWave; ++p) {
@@ -626,18 +654,26 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
         const int i = min((threadIdx.x + t * kThreads) * 4, NB * H - 4);
         xv[t] = *reinterpret_cast<const float4 *>(a.l.x + i);
       }
+      const int nch = H / kChunk;
 #pragma unroll
-      for (int t = 0; t < kXIt; ++t) {
-        const int i = (threadIdx.x + t * kThreads) * 4;
-        if (i < NB * H) *reinterpret_cast<float4 *>(xs + i) = xv[t];
+      for (int t = 0; t < kXIt; ++t) {   // float4 f of row b -> group f % 8 of chunk f / 8
+        const int i = threadIdx.x + t * kThreads;
+        if (i * 4 < NB * H) {
+          const int b = i / (H / 4), f = i - b * (H / 4);
+          reinterpret_cast<float4 *>(xs)[(b * 8 + f % 8) * nch + f / 8] = xv[t];
+        }
       }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < NB * (H / kChunk); i += kThreads) {
-      const float *p = xs + i * kChunk;
+    for (int i = threadIdx.x; i < NB * (H / kChunk); i += kThreads) {   // per-32 sums
+      const int b = i / (H / kChunk), c = i - b * (H / kChunk);
+      const ChunkX X{reinterpret_cast<const float4 *>(xs), H / kChunk, c};
       float sm = 0.0f;
 #pragma unroll
-      for (int t = 0; t < kChunk; ++t) sm += p[(t + i) & (kChunk - 1)];   // no bank conflicts
+      for (int q = 0; q < kChunk / 4; ++q) {
+        const float4 f = X(b, q);
+        sm += (f.x + f.y) + (f.z + f.w);
+      }
       xsum[i] = sm;
     }
     __syncthreads();

@@ -26,7 +26,10 @@ __device__ inline void router_rows(const RouteArgs &a, int e, int row0, int lane
   double acc[NV];
 #pragma unroll
   for (int b = 0; b < NV; ++b) acc[b] = 0.0;
-  for (int i0 = lane * 8; i0 < a.hidden; i0 += 512) {
+  // lane l takes 32-input chunks l, l + 64, ..., 8 inputs at a time: the
+  // same order (and so the same float64 sums) as the fused layer kernel
+  for (int t = 0; (lane + 64 * (t / 4)) * kChunk < a.hidden; ++t) {
+    const int i0 = (lane + 64 * (t / 4)) * kChunk + 8 * (t % 4);
     const uint4 wv = *reinterpret_cast<const uint4 *>(w + i0);
     const float wf[8] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y),
                          bf16_lo(wv.z), bf16_hi(wv.z), bf16_lo(wv.w), bf16_hi(wv.w)};
