@@ -47,6 +47,9 @@ constexpr int kRowsPerWave = 8;                       // down unit: 8 rows per w
 constexpr int kRowsPerTile = kRowsPerWave * kWaves;   // 32 rows per down tile
 constexpr int kSlotBatch = 10;                        // slots per lane per down batch
 constexpr int kStageCols = 256;                       // slot groups x slice width (= 8 x 32)
+constexpr int kStagePad = 4;                          // floats after each staged (slot, row) run of W
+// staged act floats per row of x: (slot groups x kSlotBatch) runs of W + pad, W >= 32
+constexpr int kStageFloats = kStageCols * kSlotBatch + (kStageCols / kChunk) * kSlotBatch * kStagePad;
 constexpr uint32_t kSpinLimit = 1u << 22;
 
 struct LayerArgs {
@@ -543,7 +546,7 @@ __device__ __forceinline__ void run_down(const LayerArgs &a, Shared<NB> &sh, int
         const int i = i0 + t * kThreads + threadIdx.x;
         if (i < n_f4) {
           const int q = i % (W / 4), b = (i / (W / 4)) % NB, sl = i / (W / 4) / NB;
-          *reinterpret_cast<float4 *>(act_lds + (sl * NB + b) * W + 4 * q) = f[t];
+          *reinterpret_cast<float4 *>(act_lds + (sl * NB + b) * (W + kStagePad) + 4 * q) = f[t];
         }
         const float cs = group8_sum((f[t].x + f[t].y) + (f[t].z + f[t].w));   // i = 8 chunk + (0..7)
         if (i < n_f4 && (i & 7) == 0) asum_lds[i >> 3] = cs;
@@ -558,7 +561,8 @@ __device__ __forceinline__ void run_down(const LayerArgs &a, Shared<NB> &sh, int
       const int bt = slot < n_slots ? sh.dbits[slot] : 0;
       if (bt == 0) continue;
       float P[NB];
-      const LdsX ax{act_lds + sl * NB * W + c * kChunk, W};
+      // runs of W + 4 floats: the slot groups of a row read different banks
+      const LdsX ax{act_lds + sl * NB * (W + kStagePad) + c * kChunk, W + kStagePad};
       if (bt == 4) chunk_dot<4, NB>(w[m], ax, P);
       else if (bt == 3) chunk_dot<3, NB>(w[m], ax, P);
       else chunk_dot<2, NB>(w[m], ax, P);
@@ -626,8 +630,8 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
   float *xs = reinterpret_cast<float *>(dyn);           // [NB][H]
   float *xsum = xs + NB * H;                            // [NB][H/32]
   float *keys = xsum + NB * (H / kChunk);               // routing build scratch
-  float *act_lds = xs;                                  // [batch slots][NB][W]
-  float *asum_lds = act_lds + kStageCols * kSlotBatch * NB;   // [batch slots][NB][W/32]
+  float *act_lds = xs;                                  // [batch slots][NB][W + pad]
+  float *asum_lds = act_lds + kStageFloats * NB;       // [batch slots][NB][W/32]
 
   const int x = blockIdx.x % kSlices, lr = blockIdx.x / kSlices;
   const int P = a.per_slice;
@@ -726,7 +730,7 @@ size_t dyn_lds_bytes(int nb, int hidden) {
   // and their sums
   const size_t xk = sizeof(float) * (size_t(nb) * hidden + size_t(nb) * (hidden / kChunk)) +
                     size_t(nb) * kMaxExperts * (8 + 8 + 4 + 4 + 4);
-  const size_t st = sizeof(float) * (size_t(kStageCols) * kSlotBatch * nb + size_t(8) * kSlotBatch * nb);
+  const size_t st = sizeof(float) * (size_t(kStageFloats) * nb + size_t(8) * kSlotBatch * nb);
   return xk > st ? xk : st;
 }
 
