@@ -702,14 +702,14 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
     const int u = sh.u;
     const int n_gu = u * a.ups;
     const int n_total = n_gu + a.tiles;
-    for (int i = ((lr - R - a.ups) % P + P) % P; i < n_total; i += P) {
-      if (i < n_gu) {
-        const int slot = i / a.ups;
-        run_gate_up<NB, CPL>(a, x, sh.desc[slot], slot, i - slot * a.ups, xs, xsum);
-      } else {
-        run_down<NB>(a, sh, x, i - n_gu, act_lds, asum_lds);
-      }
+    // the block's work items i0, i0 + P, ...: gate/up units first, then down
+    // tiles (two loops, so neither carries the other's live values)
+    int i = ((lr - R - a.ups) % P + P) % P;
+    for (; i < n_gu; i += P) {
+      const int slot = i / a.ups;
+      run_gate_up<NB, CPL>(a, x, sh.desc[slot], slot, i - slot * a.ups, xs, xsum);
     }
+    for (; i < n_total; i += P) run_down<NB>(a, sh, x, i - n_gu, act_lds, asum_lds);
   }
 
   // two-level exit count; the last block out resets the counters
