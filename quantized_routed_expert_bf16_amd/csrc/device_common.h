@@ -342,22 +342,14 @@ __device__ inline T ld_dev(const T *p) {
   return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// 4 consecutive floats (16-byte aligned) with one device-coherent load.
-__device__ inline float4 ld_dev_f4(const float *p) {
+// 4 consecutive floats at byte offset `off` (16-byte aligned) from `base`,
+// with one device-coherent load.  `base` must be the same in every lane: the
+// buffer descriptor lives in scalar registers, and a per-lane base would make
+// the compiler issue the load once per distinct lane value.
+__device__ inline float4 ld_dev_f4(const float *base, uint32_t off) {
   const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), (short)0, 16, 0x00020000);
-  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 16));
-}
-
-// 32 consecutive floats (16-byte aligned) with device-coherent loads.
-__device__ inline void ld_dev_32f(const float *p, float (&v)[kChunk]) {
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), (short)0, kChunk * 4, 0x00020000);
-#pragma unroll
-  for (int q = 0; q < kChunk / 4; ++q) {
-    const float4 f = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, q * 16, 0, 16));
-    v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
-  }
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, 0x7fffffff, 0x00020000);
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16));
 }
 
 // All of this block's prior stores are complete before thread 0 signals.

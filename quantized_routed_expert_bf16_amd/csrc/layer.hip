@@ -536,7 +536,7 @@ __device__ __forceinline__ void run_down(const LayerArgs &a, Shared<NB> &sh, int
         const int q = i % (W / 4), b = (i / (W / 4)) % NB, sl = i / (W / 4) / NB;
         const int slot = s0 + sl;
         const int ps = slot < u ? slot : kSharedSlot;
-        f[t] = ld_dev_f4(a.l.act + (size_t(ps) * kMaxNb + b) * I + x * W + 4 * q);
+        f[t] = ld_dev_f4(a.l.act, uint32_t(((ps * kMaxNb + b) * I + x * W + 4 * q) * 4));
       }
 #pragma unroll
       for (int t = 0; t < kStIt; ++t)
