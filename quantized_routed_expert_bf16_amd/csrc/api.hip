@@ -64,7 +64,7 @@ WorkspaceLayout workspace_layout(int hidden, int inter, int n_experts, int top_k
   };
   const int pf_rows = rows > MOE_MAX_NB ? rows : MOE_MAX_NB;
   w.counters = take(kSyncWords * sizeof(uint32_t));
-  w.act = take(size_t(kSlotStride) * kMaxNb * inter * sizeof(float));
+  w.act = take(size_t(kSlotStride) * kMaxNb * inter * sizeof(uint64_t));
   w.opart = take(size_t(kSlices) * kMaxNb * hidden * sizeof(uint64_t));
   w.slice_logits = take(size_t(kSlices) * kMaxNb * kMaxExperts * sizeof(double) +
                         size_t(kSlices) * kMaxNb * sizeof(float));
@@ -251,7 +251,7 @@ int moe_layer_forward(const float *x, int32_t nb, const moe_router *router, moe_
   l.ids = slots->ids;
   l.out = out;
   l.sync = reinterpret_cast<uint32_t *>(ws + L.counters);
-  l.act = reinterpret_cast<float *>(ws + L.act);
+  l.act = reinterpret_cast<uint64_t *>(ws + L.act);
   l.opart = reinterpret_cast<uint64_t *>(ws + L.opart);
   l.slice_logits = reinterpret_cast<double *>(ws + L.slice_logits);
   l.slice_gamma = reinterpret_cast<float *>(ws + L.slice_logits +

@@ -352,6 +352,20 @@ __device__ inline float4 ld_dev_f4(const float *base, uint32_t off) {
   return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16));
 }
 
+// Two consecutive 64-bit words at byte offset `off` (16-byte aligned) from a
+// lane-uniform `base`, with one device-coherent load; each word is read whole.
+__device__ inline void ld_dev_u64x2(const uint64_t *base, uint32_t off, uint64_t &w0, uint64_t &w1) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t *>(base), (short)0, 0x7fffffff, 0x00020000);
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16);
+  w0 = uint64_t(v[0]) | (uint64_t(v[1]) << 32);
+  w1 = uint64_t(v[2]) | (uint64_t(v[3]) << 32);
+}
+
+__device__ inline uint64_t tag_f32(uint32_t epoch, float v) {
+  return (uint64_t(epoch) << 32) | __float_as_uint(v);
+}
+
 // All of this block's prior stores are complete before thread 0 signals.
 __device__ inline void block_signal(uint32_t *counter, uint32_t inc, uint32_t *prev_out = nullptr) {
   __builtin_amdgcn_s_waitcnt(0);

@@ -367,7 +367,7 @@ __device__ __forceinline__ void build_routing(const LayerArgs &a, Shared<NB> &s,
 // 32-code chunk of the H inputs (CPL chunks when H > 2048).
 template <int NB, int CPL, int BITS>
 __device__ __forceinline__ void gate_up_unit(const LayerArgs &a, const uint8_t *rec, int j0, int act_slot,
-                             const float *xs, const float *xsum) {
+                             const float *xs, const float *xsum, uint32_t ep) {
   const int lane = threadIdx.x & 63;
   const int H = a.l.hidden, I = a.l.inter;
   const RecordLayout L = record_layout(H, I, BITS);
@@ -453,29 +453,34 @@ __device__ __forceinline__ void gate_up_unit(const LayerArgs &a, const uint8_t *
       const float gs = wave_sum(v[p][0][b]), us = wave_sum(v[p][1][b]);
       if (lane == b) { g = gs; u = us; }
     }
-    if (lane < NB) st_dev(a.l.act + (size_t(act_slot) * kMaxNb + lane) * I + j0 + p, silu_mul(g, u));
+    if (lane < NB) st_dev(a.l.act + (size_t(act_slot) * kMaxNb + lane) * I + j0 + p, tag_f32(ep, silu_mul(g, u)));
   }
 }
 
+// A gate/up unit publishes its act values tagged with the call's epoch and
+// bumps the slice counter without waiting for the stores: the counter tells
+// the down tiles when to look, the tags tell them what is current.
 template <int NB, int CPL>
 __device__ __forceinline__ void run_gate_up(const LayerArgs &a, int x, uint64_t desc, int act_slot, int unit,
-                            const float *xs, const float *xsum) {
+                            const float *xs, const float *xsum, uint32_t ep) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j0 = x * a.W + unit * kTileRowPairs + wave * kPairsPerWave;
   if (record_ok(desc, a.l.pool_bytes, a.l.hidden, a.l.inter)) {
     const uint8_t *rec = a.l.pool + (desc & ~uint64_t(255));
     switch (bits_of_tag(desc)) {
-      case 4: gate_up_unit<NB, CPL, 4>(a, rec, j0, act_slot, xs, xsum); break;
-      case 3: gate_up_unit<NB, CPL, 3>(a, rec, j0, act_slot, xs, xsum); break;
-      default: gate_up_unit<NB, CPL, 2>(a, rec, j0, act_slot, xs, xsum); break;
+      case 4: gate_up_unit<NB, CPL, 4>(a, rec, j0, act_slot, xs, xsum, ep); break;
+      case 3: gate_up_unit<NB, CPL, 3>(a, rec, j0, act_slot, xs, xsum, ep); break;
+      default: gate_up_unit<NB, CPL, 2>(a, rec, j0, act_slot, xs, xsum, ep); break;
     }
   } else {
     if (threadIdx.x == 0) set_status(a, 1u);
     if (lane < NB * kPairsPerWave)
       st_dev(a.l.act + (size_t(act_slot) * kMaxNb + lane / kPairsPerWave) * a.l.inter + j0 +
-                 lane % kPairsPerWave, 0.0f);
+                 lane % kPairsPerWave, tag_f32(ep, 0.0f));
   }
-  block_signal(sw(a, x, kSliceGu), 1u);
+  __syncthreads();   // every wave has issued its stores
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(sw(a, x, kSliceGu), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ----------------------------------------------------------------- down
@@ -529,18 +534,46 @@ __device__ __forceinline__ void run_down(const LayerArgs &a, Shared<NB> &sh, int
     __syncthreads();
     constexpr int kStIt = 4;   // loads in flight per thread
     for (int i0 = 0; i0 < n_f4; i0 += kStIt * kThreads) {
-      float4 f[kStIt];
+      uint64_t v[kStIt][4];
+      uint32_t off[kStIt];
 #pragma unroll
-      for (int t = 0; t < kStIt; ++t) {   // unconditional loads keep f in registers
+      for (int t = 0; t < kStIt; ++t) {   // unconditional loads keep v in registers
         const int i = min(i0 + t * kThreads + int(threadIdx.x), n_f4 - 1);
         const int q = i % (W / 4), b = (i / (W / 4)) % NB, sl = i / (W / 4) / NB;
         const int slot = s0 + sl;
         const int ps = slot < u ? slot : kSharedSlot;
-        f[t] = ld_dev_f4(a.l.act, uint32_t(((ps * kMaxNb + b) * I + x * W + 4 * q) * 4));
+        off[t] = uint32_t(((ps * kMaxNb + b) * I + x * W + 4 * q) * 8);
+        ld_dev_u64x2(a.l.act, off[t], v[t][0], v[t][1]);
+        ld_dev_u64x2(a.l.act, off[t] + 16, v[t][2], v[t][3]);
       }
+      // values of an earlier call (the counter can run ahead of the stores)
+      // are read again, boundedly
+      for (uint32_t it = 1;; ++it) {
+        bool stale = false;
+#pragma unroll
+        for (int t = 0; t < kStIt; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) stale |= uint32_t(v[t][e] >> 32) != sh.ep;
+        if (!stale) break;
+        if ((it & 63) == 0 && (ld_dev(a.l.sync + kSyncAbort) || it > kSpinLimit)) {
+          st_dev(a.l.sync + kSyncAbort, 1u);
+          set_status(a, 4u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+        for (int t = 0; t < kStIt; ++t) {
+          ld_dev_u64x2(a.l.act, off[t], v[t][0], v[t][1]);
+          ld_dev_u64x2(a.l.act, off[t] + 16, v[t][2], v[t][3]);
+        }
+      }
+      float4 f[kStIt];
 #pragma unroll
       for (int t = 0; t < kStIt; ++t)
-        if (i0 + t * kThreads + int(threadIdx.x) >= n_f4) f[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+        f[t] = i0 + t * kThreads + int(threadIdx.x) < n_f4
+                   ? make_float4(__uint_as_float(uint32_t(v[t][0])), __uint_as_float(uint32_t(v[t][1])),
+                                 __uint_as_float(uint32_t(v[t][2])), __uint_as_float(uint32_t(v[t][3])))
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int t = 0; t < kStIt; ++t) {
         const int i = i0 + t * kThreads + threadIdx.x;
@@ -695,7 +728,7 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
     }
     // the shared expert's gate/up units need no routing
     for (int i = ((lr - R) % P + P) % P; i < a.ups; i += P)
-      run_gate_up<NB, CPL>(a, x, a.l.shared_rec, kSharedSlot, i, xs, xsum);
+      run_gate_up<NB, CPL>(a, x, a.l.shared_rec, kSharedSlot, i, xs, xsum, sh.ep);
 
     wait_geq(a, sw(a, x, kSliceRoute), uint32_t(a.route_blocks));
     build_routing<NB>(a, sh, lg, gm, rec_lds, reinterpret_cast<uint8_t *>(keys));
@@ -707,7 +740,7 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
     int i = ((lr - R - a.ups) % P + P) % P;
     for (; i < n_gu; i += P) {
       const int slot = i / a.ups;
-      run_gate_up<NB, CPL>(a, x, sh.desc[slot], slot, i - slot * a.ups, xs, xsum);
+      run_gate_up<NB, CPL>(a, x, sh.desc[slot], slot, i - slot * a.ups, xs, xsum, sh.ep);
     }
     for (; i < n_total; i += P) run_down<NB>(a, sh, x, i - n_gu, act_lds, asum_lds);
   }

@@ -86,7 +86,7 @@ struct LayerLaunch {
   uint32_t *ids;             // [64]
   float *out;                // [nb][H]
   uint32_t *sync;            // 256 counter words (workspace head)
-  float *act;                // [64][4][I]
+  uint64_t *act;             // [64][4][I]  epoch << 32 | f32 bits
   uint64_t *opart;           // [8][4][H]  per-slice partial outputs: epoch << 32 | f32 bits
   double *slice_logits;      // [8][4][256] per-slice router logits
   float *slice_gamma;        // [8][4]
@@ -95,7 +95,7 @@ struct LayerLaunch {
 // Workspace layout (decode and prefill share the head).
 struct WorkspaceLayout {
   size_t counters;     // kSyncWords u32 counter / status words
-  size_t act;          // decode: [64][4][I] f32
+  size_t act;          // decode: [64][4][I] epoch-tagged f32
   size_t opart;        // decode: [8][4][H] per-slice partial outputs (epoch-tagged f32)
   size_t slice_logits; // decode: [8][4][256] f64, [8][4] f32 gamma after it
   size_t pf_xf;        // prefill: [2 orders][hi, lo][32][H] f16 MFMA-ordered x
