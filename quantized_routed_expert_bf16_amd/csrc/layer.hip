@@ -92,7 +92,6 @@ __device__ inline void wait_geq(const LayerArgs &a, const uint32_t *p, uint32_t 
 template <int NB>
 struct Shared {
   double exq[64];
-  int ncand;
   int sel[NB][kMaxTopK];
   double selv[NB][kMaxTopK];
   float wsel[NB][kMaxTopK];
@@ -182,146 +181,127 @@ __device__ __forceinline__ void router_rows(const LayerArgs &a, const float *xs,
   }
 }
 
-// Top-k, weights and union of the slice's published logits (every block).
-// The order is (logit descending, id ascending) on 64-bit order-preserving
-// keys of the float64 logits.  Step 1 counts, for every (row, expert), the
-// experts of its row with a larger high key word (32-bit compares, split
-// over adjacent lanes and merged with DPP); only entries with fewer than k
-// such experts can be selected, and any two entries whose high words tie
-// are both among them.  Step 2 (wave 0) completes the exact rank of those
-// candidates against each other, then takes the softmax of each row's k
-// selected logits, the first-seen union of the (row, rank) list and the
-// per-slot record pointers used by the expert units.
+// Top-k, weights and union of the published logits (every block).  Wave b
+// (b < NB) holds row b's logits in registers, expert lane + 64 j in register
+// j, with 64-bit order-preserving keys of the float64 values.  A most-
+// significant-bit-first radix select (ballot counts) finds the longest key
+// prefix T that at least k keys reach; it stops early once exactly k do.
+// Keys above T are selected and, of the keys equal to T (equal logits), the
+// lowest ids fill the remaining places, which is the order (logit
+// descending, id ascending).  The k entries are packed into LDS in id order,
+// ranked against each other and given their softmax weights.  Wave 0 then
+// builds the first-seen union of the (row, rank) list and the per-slot
+// record pointers used by the expert units.
 template <int NB>
 __device__ __forceinline__ void build_routing(const LayerArgs &a, Shared<NB> &s, const double *lg, const float *gm,
                               const uint64_t *rec_lds, uint8_t *kbuf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int E = a.l.n_experts, k = a.l.top_k;
-  const int Ep = (E + 15) & ~15;
-  uint64_t *key = reinterpret_cast<uint64_t *>(kbuf);                       // [NB][Ep]
-  double *val = reinterpret_cast<double *>(kbuf) + NB * kMaxExperts;        // [NB][Ep]
-  uint32_t *khi = reinterpret_cast<uint32_t *>(val + NB * kMaxExperts);     // [NB][Ep]
-  int *cand = reinterpret_cast<int *>(khi + NB * kMaxExperts);              // candidate position
-  int *cgt = cand + NB * kMaxExperts;                                       // its step-1 count
-  {   // all of the thread's logit loads in flight at once
-    constexpr int kIt = NB * kMaxExperts / kThreads;
-    double lv[kIt];
+  constexpr int kJ = kMaxExperts / 64;
+  if (wave < NB) {
+    const int b = wave;
+    uint64_t *ck = reinterpret_cast<uint64_t *>(kbuf) + b * 16;                 // [NB][16] keys
+    double *cv = reinterpret_cast<double *>(kbuf) + NB * 16 + b * 16;           // values
+    int *cid = reinterpret_cast<int *>(reinterpret_cast<double *>(kbuf) + 2 * NB * 16) + b * 16;   // ids
+    double v[kJ];
 #pragma unroll
-    for (int t = 0; t < kIt; ++t) {   // unconditional loads keep lv in registers
-      const int p = threadIdx.x + t * kThreads, b = p / Ep, e = p - b * Ep;
-      const bool in = p < NB * Ep && e < E;
-      lv[t] = ld_dev(lg + (in ? b * kMaxExperts + e : 0));
+    for (int j = 0; j < kJ; ++j)   // clamped and unconditional: all loads in flight at once
+      v[j] = ld_dev(lg + b * kMaxExperts + min(lane + 64 * j, E - 1));
+    const float gam = ld_dev(gm + b);
+    uint64_t kk[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      // + 0.0 folds -0 into +0 so that equal logits tie on the id alone;
+      // padding keys are 0, below every finite logit's key and below every
+      // prefix the select tries
+      const bool in = lane + 64 * j < E;
+      kk[j] = in ? order_key(v[j] + 0.0) : 0;
     }
+    uint64_t T = 0;
+    int cnt = kJ * 64;   // keys >= T
+    for (int bit = 63; bit >= 0 && cnt != k; --bit) {
+      const uint64_t c = T | (uint64_t(1) << bit);
+      int n = 0;
 #pragma unroll
-    for (int t = 0; t < kIt; ++t) {
-      const int p = threadIdx.x + t * kThreads, e = p % Ep;
-      if (p < NB * Ep) {
-        // + 0.0 folds -0 into +0 so that equal logits tie on the id alone;
-        // padding keys are 0, below every finite logit's key
-        const double v = e < E ? lv[t] + 0.0 : 0.0;
-        const uint64_t kk = e < E ? order_key(v) : 0;
-        key[p] = kk;
-        val[p] = v;
-        khi[p] = uint32_t(kk >> 32);
+      for (int j = 0; j < kJ; ++j) n += __popcll(__ballot(kk[j] >= c));
+      if (n >= k) {
+        T = c;
+        cnt = n;
       }
     }
-  }
-  if (threadIdx.x < NB) s.gam[threadIdx.x] = ld_dev(gm + threadIdx.x);
-  if (threadIdx.x == 0) s.ncand = 0;
-  __syncthreads();
-
-  // step 1: S = 2^lg_s adjacent lanes per entry, each over Ep / S keys
-  const int items = NB * E;
-  const int lg_s = 4 * items <= kThreads ? 2 : (2 * items <= kThreads ? 1 : 0);
-  const int quads = (Ep >> lg_s) >> 2;
-  for (int base = 0; base < (items << lg_s); base += kThreads) {
-    const int t = base + threadIdx.x;
-    const int p = t >> lg_s, h = t & ((1 << lg_s) - 1);
-    int gt = 0, b = 0, e = 0;
-    if (p < items) {
-      b = p / E;
-      e = p - b * E;
-      const uint32_t kh = khi[b * Ep + e];
-      const uint4 *row = reinterpret_cast<const uint4 *>(khi + b * Ep) + h * quads;
-#pragma unroll 8
-      for (int f = 0; f < quads; ++f) {
-        const uint4 o = row[f];
-        gt += (int(o.x > kh) + int(o.y > kh)) + (int(o.z > kh) + int(o.w > kh));
+    int need = k;   // places left for keys equal to T
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) need -= __popcll(__ballot(kk[j] > T));
+    const uint64_t below = (uint64_t(1) << lane) - 1;
+    int eq_before = 0, packed = 0;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const bool eq = kk[j] == T;
+      const uint64_t eqm = __ballot(eq);
+      const bool take = kk[j] > T || (eq && eq_before + __popcll(eqm & below) < need);
+      const uint64_t tm = __ballot(take);
+      if (take) {
+        const int ci = packed + __popcll(tm & below);
+        ck[ci] = kk[j];
+        cv[ci] = v[j] + 0.0;
+        cid[ci] = lane + 64 * j;
       }
+      eq_before += __popcll(eqm);
+      packed += __popcll(tm);
     }
-    if (lg_s >= 1) gt += __builtin_amdgcn_mov_dpp(gt, 0xB1, 0xF, 0xF, true);   // xor 1
-    if (lg_s >= 2) gt += __builtin_amdgcn_mov_dpp(gt, 0x4E, 0xF, 0xF, true);   // xor 2
-    if (p < items && h == 0 && gt < k) {
-      const int j = atomicAdd(&s.ncand, 1);
-      cand[j] = b * Ep + e;
-      cgt[j] = gt;
+    __builtin_amdgcn_wave_barrier();
+    // rank of packed entry `lane` (LDS accesses of one wave complete in
+    // order, so the wave reads back what its lanes wrote)
+    const bool me = lane < k;
+    const uint64_t mk = ck[me ? lane : 0];
+    const int mid = cid[me ? lane : 0];
+    const double mv = cv[me ? lane : 0];
+    int rank = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxTopK; ++q)
+      if (q < k) rank += int(pair_before(ck[q], cid[q], mk, mid));
+    if (me) {
+      s.sel[b][rank] = mid;
+      s.selv[b][rank] = mv;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // softmax of the row's k selected logits, summed in rank order
+    const double ex = me ? exp(mv - s.selv[b][0]) : 0.0;
+    if (me) s.exq[b * k + rank] = ex;
+    __builtin_amdgcn_wave_barrier();
+    double sum = 0.0;
+    for (int r = 0; r < k; ++r) sum += s.exq[b * k + r];
+    if (me) s.wsel[b][rank] = float(ex / sum);
+    if (lane == 0) s.gam[b] = gam;
+    if (blockIdx.x == 0) {   // caller-visible logits (as published)
+#pragma unroll
+      for (int j = 0; j < kJ; ++j)
+        if (lane + 64 * j < E) a.l.logits[b * E + lane + 64 * j] = v[j];
     }
   }
   __syncthreads();
 
   if (wave == 0) {
-    // step 2: exact ranks of the candidates (LDS accesses of one wave
-    // complete in order, so the wave reads back what its lanes wrote)
-    const int nc = s.ncand;
-    if (nc <= 64) {   // lane q holds candidate q; the others come by readlane
-      const bool cq = lane < nc;
-      const int pos = cq ? cand[lane] : 0;
-      const uint64_t kk = cq ? key[pos] : 0;
-      int rank = cq ? cgt[lane] : 0;
-      const int r0 = (pos / Ep) * Ep;
-      for (int q = 0; q < nc; ++q) {
-        const int pq = __builtin_amdgcn_readlane(pos, q);
-        const uint64_t kq = readlane_u64(kk, q);
-        rank += int(pq >= r0 && pq < r0 + Ep && (kq >> 32) == (kk >> 32) &&
-                    (kq > kk || (kq == kk && pq < pos)));
-      }
-      if (cq && rank < k) {
-        s.sel[pos / Ep][rank] = pos - r0;
-        s.selv[pos / Ep][rank] = val[pos];
-      }
-    } else {          // many tied high words: candidates from LDS
-      for (int j = lane; j < nc; j += 64) {
-        const int pos = cand[j];
-        const int r0 = (pos / Ep) * Ep;
-        const uint64_t kk = key[pos];
-        int rank = cgt[j];
-        for (int q = 0; q < nc; ++q) {
-          const int pq = cand[q];
-          const uint64_t kq = key[pq];
-          rank += int(pq >= r0 && pq < r0 + Ep && (kq >> 32) == (kk >> 32) &&
-                      (kq > kk || (kq == kk && pq < pos)));
-        }
-        if (rank < k) {
-          s.sel[pos / Ep][rank] = pos - r0;
-          s.selv[pos / Ep][rank] = val[pos];
-        }
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
     // lane l < NB k holds entry (row l / k, rank l % k)
     const int n = NB * k;
     const bool ent = lane < n;
     const int lb = ent ? lane / k : 0, lr = lane - lb * k;
     const int e_l = ent ? s.sel[lb][lr] : 0;
+    const float w_l = ent ? s.wsel[lb][lr] : 0.0f;
     const uint64_t d_l = ent ? rec_lds[e_l] : a.l.shared_rec;
-    const double ex = ent ? exp(s.selv[lb][lr] - s.selv[lb][0]) : 0.0;
-    s.exq[lane] = ex;
-    // first-seen union: fq = lowest entry with this lane's expert
+    // first-seen union: fq = lowest entry with this lane's expert (a row's
+    // k experts are distinct, so one row needs no search)
     int fq = lane;
-    for (int q = 0; q < n; ++q) {
-      const int eq = __builtin_amdgcn_readlane(e_l, q);
-      fq = (eq == e_l && q < fq) ? q : fq;
+    if constexpr (NB > 1) {
+      for (int q = 0; q < n; ++q) {
+        const int eq = __builtin_amdgcn_readlane(e_l, q);
+        fq = (eq == e_l && q < fq) ? q : fq;
+      }
     }
     const bool first = ent && fq == lane;
     const uint64_t mask = __ballot(first);
     const int slot = __popcll(mask & ((uint64_t(1) << fq) - 1));
     const int u = __popcll(mask);
-    __builtin_amdgcn_wave_barrier();
-    // softmax of each row's k selected logits
-    double sum = 0.0;
-    for (int r = 0; r < k; ++r) sum += s.exq[lb * k + r];
-    const float w_l = ent ? float(ex / sum) : 0.0f;
-    if (ent) s.wsel[lb][lr] = w_l;
     if (lane == 0) s.u = u;
 #pragma unroll
     for (int b = 0; b < NB; ++b) s.wslot[b][lane] = lane == u ? s.gam[b] : 0.0f;
@@ -356,8 +336,6 @@ __device__ __forceinline__ void build_routing(const LayerArgs &a, Shared<NB> &s,
       a.l.topk_idx[p] = uint32_t(s.sel[p / k][p % k]);
       a.l.topk_w[p] = s.wsel[p / k][p % k];
     }
-    for (int p = threadIdx.x; p < NB * E; p += kThreads)
-      a.l.logits[p] = ld_dev(lg + (p / E) * kMaxExperts + p % E);
     if (threadIdx.x < NB) a.l.gamma[threadIdx.x] = s.gam[threadIdx.x];
   }
 }
