@@ -35,6 +35,7 @@ __device__ inline bool record_ok(uint64_t desc, uint64_t pool_bytes, int hidden,
 
 // Codes of one 32-code chunk of a packed row: 4-bit: w[0..3] (16 B);
 // 2-bit: w[0..1] (8 B); 3-bit: w[0..1] low plane, w[2] high plane (8 + 4 B).
+// Words a width does not use are left as they are (no decoder reads them).
 template <int BITS>
 __device__ inline void load_chunk(const uint8_t *row, int row_codes, int chunk, uint32_t (&w)[4]) {
   if constexpr (BITS == 4) {
@@ -42,12 +43,11 @@ __device__ inline void load_chunk(const uint8_t *row, int row_codes, int chunk, 
     w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
   } else if constexpr (BITS == 2) {
     const uint2 v = *reinterpret_cast<const uint2 *>(row + chunk * 8);
-    w[0] = v.x; w[1] = v.y; w[2] = 0; w[3] = 0;
+    w[0] = v.x; w[1] = v.y;
   } else {
     const uint2 v = *reinterpret_cast<const uint2 *>(row + chunk * 8);
     w[0] = v.x; w[1] = v.y;
     w[2] = *reinterpret_cast<const uint32_t *>(row + row_codes / 4 + chunk * 4);
-    w[3] = 0;
   }
 }
 

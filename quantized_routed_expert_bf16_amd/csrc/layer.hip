@@ -46,6 +46,7 @@ constexpr int kPairsPerWave = kTileRowPairs / kWaves;
 constexpr int kRowsPerWave = 8;                       // down unit: 8 rows per wave
 constexpr int kRowsPerTile = kRowsPerWave * kWaves;   // 32 rows per down tile
 constexpr int kSlotBatch = 10;                        // slots per lane per down batch
+constexpr int kWaitVm0 = 0x0F70;                      // s_waitcnt vmcnt(0) only
 constexpr int kStageCols = 256;                       // slot groups x slice width (= 8 x 32)
 constexpr int kStagePad = 4;                          // floats after each staged (slot, row) run of W
 // staged act floats per row of x: (slot groups x kSlotBatch) runs of W + pad, W >= 32
@@ -181,20 +182,18 @@ __device__ __forceinline__ void router_rows(const LayerArgs &a, const float *xs,
   }
 }
 
-// Top-k, weights and union of the published logits (every block).  Wave b
-// (b < NB) holds row b's logits in registers, expert lane + 64 j in register
-// j, with 64-bit order-preserving keys of the float64 values.  A most-
-// significant-bit-first radix select (ballot counts) finds the longest key
-// prefix T that at least k keys reach; it stops early once exactly k do.
-// Keys above T are selected and, of the keys equal to T (equal logits), the
-// lowest ids fill the remaining places, which is the order (logit
-// descending, id ascending).  The k entries are packed into LDS in id order,
-// ranked against each other and given their softmax weights.  Wave 0 then
-// builds the first-seen union of the (row, rank) list and the per-slot
-// record pointers used by the expert units.
+// Top-k of the published logits (every block).  Wave b (b < NB) holds row
+// b's logits in registers, expert lane + 64 j in register j, with 64-bit
+// order-preserving keys of the float64 values.  A most-significant-bit-first
+// radix select (ballot counts) finds the longest key prefix T that at least
+// k keys reach; it stops early once exactly k do.  Keys above T are selected
+// and, of the keys equal to T (equal logits), the lowest ids fill the
+// remaining places, which is the order (logit descending, id ascending).
+// The k entries are packed into LDS in id order and ranked against each
+// other: s.sel[b][rank] and s.selv[b][rank] on return, for every wave.
 template <int NB>
-__device__ __forceinline__ void build_routing(const LayerArgs &a, Shared<NB> &s, const double *lg, const float *gm,
-                              const uint64_t *rec_lds, uint8_t *kbuf) {
+__device__ __forceinline__ void route_select(const LayerArgs &a, Shared<NB> &s, const double *lg, const float *gm,
+                             uint8_t *kbuf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int E = a.l.n_experts, k = a.l.top_k;
   constexpr int kJ = kMaxExperts / 64;
@@ -264,14 +263,6 @@ __device__ __forceinline__ void build_routing(const LayerArgs &a, Shared<NB> &s,
       s.sel[b][rank] = mid;
       s.selv[b][rank] = mv;
     }
-    __builtin_amdgcn_wave_barrier();
-    // softmax of the row's k selected logits, summed in rank order
-    const double ex = me ? exp(mv - s.selv[b][0]) : 0.0;
-    if (me) s.exq[b * k + rank] = ex;
-    __builtin_amdgcn_wave_barrier();
-    double sum = 0.0;
-    for (int r = 0; r < k; ++r) sum += s.exq[b * k + r];
-    if (me) s.wsel[b][rank] = float(ex / sum);
     if (lane == 0) s.gam[b] = gam;
     if (blockIdx.x == 0) {   // caller-visible logits (as published)
 #pragma unroll
@@ -280,17 +271,26 @@ __device__ __forceinline__ void build_routing(const LayerArgs &a, Shared<NB> &s,
     }
   }
   __syncthreads();
+}
 
+// Softmax weights of each row's k selected logits, the first-seen union of
+// the (row, rank) list and the per-slot record pointers used by the expert
+// units (wave 0; every wave on return).  A row's k experts are distinct, so
+// union slot s < k is always row 0's rank-s expert.
+template <int NB>
+__device__ __forceinline__ void route_union(const LayerArgs &a, Shared<NB> &s, const uint64_t *rec_lds) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int k = a.l.top_k;
   if (wave == 0) {
     // lane l < NB k holds entry (row l / k, rank l % k)
     const int n = NB * k;
     const bool ent = lane < n;
     const int lb = ent ? lane / k : 0, lr = lane - lb * k;
     const int e_l = ent ? s.sel[lb][lr] : 0;
-    const float w_l = ent ? s.wsel[lb][lr] : 0.0f;
     const uint64_t d_l = ent ? rec_lds[e_l] : a.l.shared_rec;
-    // first-seen union: fq = lowest entry with this lane's expert (a row's
-    // k experts are distinct, so one row needs no search)
+    const double ex = ent ? exp(s.selv[lb][lr] - s.selv[lb][0]) : 0.0;
+    s.exq[lane] = ex;
+    // first-seen union: fq = lowest entry with this lane's expert
     int fq = lane;
     if constexpr (NB > 1) {
       for (int q = 0; q < n; ++q) {
@@ -302,6 +302,12 @@ __device__ __forceinline__ void build_routing(const LayerArgs &a, Shared<NB> &s,
     const uint64_t mask = __ballot(first);
     const int slot = __popcll(mask & ((uint64_t(1) << fq) - 1));
     const int u = __popcll(mask);
+    __builtin_amdgcn_wave_barrier();
+    // softmax of each row's k selected logits, summed in rank order
+    double sum = 0.0;
+    for (int r = 0; r < k; ++r) sum += s.exq[lb * k + r];
+    const float w_l = ent ? float(ex / sum) : 0.0f;
+    if (ent) s.wsel[lb][lr] = w_l;
     if (lane == 0) s.u = u;
 #pragma unroll
     for (int b = 0; b < NB; ++b) s.wslot[b][lane] = lane == u ? s.gam[b] : 0.0f;
@@ -343,35 +349,54 @@ __device__ __forceinline__ void build_routing(const LayerArgs &a, Shared<NB> &s,
 // ------------------------------------------------------------ gate / up
 // 8 row pairs (gate j, up j) of one slot; each wave takes 2, a lane one
 // 32-code chunk of the H inputs (CPL chunks when H > 2048).
-template <int NB, int CPL, int BITS>
-__device__ __forceinline__ void gate_up_unit(const LayerArgs &a, const uint8_t *rec, int j0, int act_slot,
-                             const float *xs, const float *xsum, uint32_t ep) {
+// The lane's codes and (scale, bias) words of a unit's row pairs.
+template <int CPL>
+struct GuRegs {
+  uint32_t w[kPairsPerWave][2][CPL][4];
+  uint32_t s[kPairsPerWave][2][CPL];
+};
+
+template <int CPL, int BITS>
+__device__ __forceinline__ void gate_up_load(const LayerArgs &a, const uint8_t *rec, int j0, GuRegs<CPL> &r) {
   const int lane = threadIdx.x & 63;
   const int H = a.l.hidden, I = a.l.inter;
   const RecordLayout L = record_layout(H, I, BITS);
   const int n_chunks = H / kChunk, gpr = H / kGroup;
   const uint8_t *codes = rec + L.gu_codes;
   const uint32_t *sb = reinterpret_cast<const uint32_t *>(rec + L.gu_sb);
-
-  uint32_t w[kPairsPerWave][2][CPL][4];
-  uint32_t s[kPairsPerWave][2][CPL];
 #pragma unroll
   for (int p = 0; p < kPairsPerWave; ++p)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int row = 2 * (j0 + p) + h;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const int chunk = lane + 64 * c;
-        if (chunk < n_chunks) {
-          load_chunk<BITS>(codes + size_t(row) * L.gu_row_bytes, H, chunk, w[p][h][c]);
-          s[p][h][c] = sb[size_t(row) * gpr + chunk / 2];
-        } else {
-          w[p][h][c][0] = w[p][h][c][1] = w[p][h][c][2] = w[p][h][c][3] = 0;
-          s[p][h][c] = 0;
-        }
+      for (int c = 0; c < CPL; ++c) {   // clamped, unconditional (lanes past H drop out later)
+        const int chunk = min(lane + 64 * c, n_chunks - 1);
+        load_chunk<BITS>(codes + size_t(row) * L.gu_row_bytes, H, chunk, r.w[p][h][c]);
+        r.s[p][h][c] = sb[size_t(row) * gpr + chunk / 2];
       }
     }
+}
+
+// Loads for a record of any bit width (the tag is uniform).
+template <int CPL>
+__device__ __forceinline__ void gate_up_load_any(const LayerArgs &a, uint64_t desc, int j0, GuRegs<CPL> &r) {
+  const uint8_t *rec = a.l.pool + (desc & ~uint64_t(255));
+  switch (bits_of_tag(desc)) {
+    case 4: gate_up_load<CPL, 4>(a, rec, j0, r); break;
+    case 3: gate_up_load<CPL, 3>(a, rec, j0, r); break;
+    default: gate_up_load<CPL, 2>(a, rec, j0, r); break;
+  }
+}
+
+template <int NB, int CPL, int BITS>
+__device__ __forceinline__ void gate_up_unit(const LayerArgs &a, const GuRegs<CPL> &r, int j0, int act_slot,
+                             const float *xs, const float *xsum, uint32_t ep) {
+  const int lane = threadIdx.x & 63;
+  const int H = a.l.hidden, I = a.l.inter;
+  const int n_chunks = H / kChunk;
+  const auto &w = r.w;
+  const auto &s = r.s;
   float v[kPairsPerWave][2][NB];
 #pragma unroll
   for (int p = 0; p < kPairsPerWave; ++p)
@@ -402,7 +427,7 @@ __device__ __forceinline__ void gate_up_unit(const LayerArgs &a, const uint8_t *
         for (int h = 0; h < 2; ++h) {
           float P[NB];
           chunk_dot<BITS, NB>(w[p][h][c], RegX<NB>{xr}, P);
-          const float sc = sb_scale(s[p][h][c]), bi = sb_bias(s[p][h][c]);
+          const float sc = live ? sb_scale(s[p][h][c]) : 0.0f, bi = live ? sb_bias(s[p][h][c]) : 0.0f;
 #pragma unroll
           for (int b = 0; b < NB; ++b) v[p][h][b] += fmaf(sc, P[b], bi * xsm[b]);
         }
@@ -417,7 +442,8 @@ __device__ __forceinline__ void gate_up_unit(const LayerArgs &a, const uint8_t *
       chunk_dot_rows<BITS, NB, R>(wr, X, P);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const float sc = sb_scale(s[r / 2][r % 2][c]), bi = sb_bias(s[r / 2][r % 2][c]);
+        const float sc = live ? sb_scale(s[r / 2][r % 2][c]) : 0.0f;
+        const float bi = live ? sb_bias(s[r / 2][r % 2][c]) : 0.0f;
 #pragma unroll
         for (int b = 0; b < NB; ++b) v[r / 2][r % 2][b] += fmaf(sc, P[r][b], bi * xsm[b]);
       }
@@ -438,17 +464,23 @@ __device__ __forceinline__ void gate_up_unit(const LayerArgs &a, const uint8_t *
 // A gate/up unit publishes its act values tagged with the call's epoch and
 // bumps the slice counter without waiting for the stores: the counter tells
 // the down tiles when to look, the tags tell them what is current.
-template <int NB, int CPL>
+// First gate/up row pair of the wave in a unit.
+__device__ __forceinline__ int gate_up_row0(const LayerArgs &a, int x, int unit) {
+  return x * a.W + unit * kTileRowPairs + (threadIdx.x >> 6) * kPairsPerWave;
+}
+
+// kLoaded: `r` already holds the unit's weights.
+template <int NB, int CPL, bool kLoaded = false>
 __device__ __forceinline__ void run_gate_up(const LayerArgs &a, int x, uint64_t desc, int act_slot, int unit,
-                            const float *xs, const float *xsum, uint32_t ep) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int j0 = x * a.W + unit * kTileRowPairs + wave * kPairsPerWave;
+                            const float *xs, const float *xsum, uint32_t ep, GuRegs<CPL> &r) {
+  const int lane = threadIdx.x & 63;
+  const int j0 = gate_up_row0(a, x, unit);
   if (record_ok(desc, a.l.pool_bytes, a.l.hidden, a.l.inter)) {
-    const uint8_t *rec = a.l.pool + (desc & ~uint64_t(255));
+    if constexpr (!kLoaded) gate_up_load_any<CPL>(a, desc, j0, r);
     switch (bits_of_tag(desc)) {
-      case 4: gate_up_unit<NB, CPL, 4>(a, rec, j0, act_slot, xs, xsum, ep); break;
-      case 3: gate_up_unit<NB, CPL, 3>(a, rec, j0, act_slot, xs, xsum, ep); break;
-      default: gate_up_unit<NB, CPL, 2>(a, rec, j0, act_slot, xs, xsum, ep); break;
+      case 4: gate_up_unit<NB, CPL, 4>(a, r, j0, act_slot, xs, xsum, ep); break;
+      case 3: gate_up_unit<NB, CPL, 3>(a, r, j0, act_slot, xs, xsum, ep); break;
+      default: gate_up_unit<NB, CPL, 2>(a, r, j0, act_slot, xs, xsum, ep); break;
     }
   } else {
     if (threadIdx.x == 0) set_status(a, 1u);
@@ -705,20 +737,43 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
                                __HIP_MEMORY_SCOPE_AGENT);
     }
     // the shared expert's gate/up units need no routing
-    for (int i = ((lr - R) % P + P) % P; i < a.ups; i += P)
-      run_gate_up<NB, CPL>(a, x, a.l.shared_rec, kSharedSlot, i, xs, xsum, sh.ep);
+    for (int i = ((lr - R) % P + P) % P; i < a.ups; i += P) {
+      GuRegs<CPL> r;
+      run_gate_up<NB, CPL>(a, x, a.l.shared_rec, kSharedSlot, i, xs, xsum, sh.ep, r);
+    }
 
     wait_geq(a, sw(a, x, kSliceRoute), uint32_t(a.route_blocks));
-    build_routing<NB>(a, sh, lg, gm, rec_lds, reinterpret_cast<uint8_t *>(keys));
+    route_select<NB>(a, sh, lg, gm, reinterpret_cast<uint8_t *>(keys));
+    // the block's work items i0, i0 + P, ...: gate/up units first, then down
+    // tiles (two loops, so neither carries the other's live values).  When
+    // the first unit's slot is one of row 0's ranks its expert is known
+    // already: its weights load while the union is built.
+    int i = ((lr - R - a.ups) % P + P) % P;
+    const int slot0 = i / a.ups;
+    GuRegs<CPL> pre;
+    const bool early = slot0 < a.l.top_k;
+    uint64_t d0 = 0;
+    // retire every older vector memory access first, so that nothing in the
+    // union build has to wait on these loads
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    if (early) {
+      d0 = rec_lds[sh.sel[0][slot0]];
+      if (record_ok(d0, a.l.pool_bytes, a.l.hidden, a.l.inter))
+        gate_up_load_any<CPL>(a, d0, gate_up_row0(a, x, i - slot0 * a.ups), pre);
+    }
+    asm volatile("" ::: "memory");   // the loads are issued here, not sunk to their use
+    route_union<NB>(a, sh, rec_lds);
     const int u = sh.u;
     const int n_gu = u * a.ups;
     const int n_total = n_gu + a.tiles;
-    // the block's work items i0, i0 + P, ...: gate/up units first, then down
-    // tiles (two loops, so neither carries the other's live values)
-    int i = ((lr - R - a.ups) % P + P) % P;
+    if (early) {   // slot0 < k <= u: a gate/up unit
+      run_gate_up<NB, CPL, true>(a, x, d0, slot0, i - slot0 * a.ups, xs, xsum, sh.ep, pre);
+      i += P;
+    }
     for (; i < n_gu; i += P) {
       const int slot = i / a.ups;
-      run_gate_up<NB, CPL>(a, x, sh.desc[slot], slot, i - slot * a.ups, xs, xsum, sh.ep);
+      GuRegs<CPL> r;
+      run_gate_up<NB, CPL>(a, x, sh.desc[slot], slot, i - slot * a.ups, xs, xsum, sh.ep, r);
     }
     for (; i < n_total; i += P) run_down<NB>(a, sh, x, i - n_gu, act_lds, asum_lds);
   }
