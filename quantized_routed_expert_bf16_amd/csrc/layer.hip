@@ -191,84 +191,94 @@ __device__ __forceinline__ void router_rows(const LayerArgs &a, const float *xs,
 // remaining places, which is the order (logit descending, id ascending).
 // The k entries are packed into LDS in id order and ranked against each
 // other: s.sel[b][rank] and s.selv[b][rank] on return, for every wave.
+// kJ = 2 serves up to 128 experts, 4 up to 256.
+template <int NB, int kJ>
+__device__ __forceinline__ void select_row(const LayerArgs &a, Shared<NB> &s, const double *lg, const float *gm,
+                           uint8_t *kbuf, int b) {
+  const int lane = threadIdx.x & 63;
+  const int E = a.l.n_experts, k = a.l.top_k;
+  uint64_t *ck = reinterpret_cast<uint64_t *>(kbuf) + b * 16;                 // [NB][16] keys
+  double *cv = reinterpret_cast<double *>(kbuf) + NB * 16 + b * 16;           // values
+  int *cid = reinterpret_cast<int *>(reinterpret_cast<double *>(kbuf) + 2 * NB * 16) + b * 16;   // ids
+  double v[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j)   // clamped and unconditional: all loads in flight at once
+    v[j] = ld_dev(lg + b * kMaxExperts + min(lane + 64 * j, E - 1));
+  const float gam = ld_dev(gm + b);
+  uint64_t kk[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    // + 0.0 folds -0 into +0 so that equal logits tie on the id alone;
+    // padding keys are 0, below every finite logit's key and below every
+    // prefix the select tries
+    const bool in = lane + 64 * j < E;
+    kk[j] = in ? order_key(v[j] + 0.0) : 0;
+  }
+  uint64_t T = 0;
+  int cnt = kJ * 64;   // keys >= T
+  for (int bit = 63; bit >= 0 && cnt != k; --bit) {
+    const uint64_t c = T | (uint64_t(1) << bit);
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) n += __popcll(__ballot(kk[j] >= c));
+    if (n >= k) {
+      T = c;
+      cnt = n;
+    }
+  }
+  int need = k;   // places left for keys equal to T
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) need -= __popcll(__ballot(kk[j] > T));
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  int eq_before = 0, packed = 0;
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const bool eq = kk[j] == T;
+    const uint64_t eqm = __ballot(eq);
+    const bool take = kk[j] > T || (eq && eq_before + __popcll(eqm & below) < need);
+    const uint64_t tm = __ballot(take);
+    if (take) {
+      const int ci = packed + __popcll(tm & below);
+      ck[ci] = kk[j];
+      cv[ci] = v[j] + 0.0;
+      cid[ci] = lane + 64 * j;
+    }
+    eq_before += __popcll(eqm);
+    packed += __popcll(tm);
+  }
+  __builtin_amdgcn_wave_barrier();
+  // rank of packed entry `lane` (LDS accesses of one wave complete in
+  // order, so the wave reads back what its lanes wrote)
+  const bool me = lane < k;
+  const uint64_t mk = ck[me ? lane : 0];
+  const int mid = cid[me ? lane : 0];
+  const double mv = cv[me ? lane : 0];
+  int rank = 0;
+#pragma unroll
+  for (int q = 0; q < kMaxTopK; ++q) {   // every read issued at once; q >= k masked
+    const uint64_t qk = ck[q];
+    const int qi = cid[q];
+    rank += int(q < k && pair_before(qk, qi, mk, mid));
+  }
+  if (me) {
+    s.sel[b][rank] = mid;
+    s.selv[b][rank] = mv;
+  }
+  if (lane == 0) s.gam[b] = gam;
+  if (blockIdx.x == 0) {   // caller-visible logits (as published)
+#pragma unroll
+    for (int j = 0; j < kJ; ++j)
+      if (lane + 64 * j < E) a.l.logits[b * E + lane + 64 * j] = v[j];
+  }
+}
+
 template <int NB>
 __device__ __forceinline__ void route_select(const LayerArgs &a, Shared<NB> &s, const double *lg, const float *gm,
                              uint8_t *kbuf) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int E = a.l.n_experts, k = a.l.top_k;
-  constexpr int kJ = kMaxExperts / 64;
+  const int wave = threadIdx.x >> 6;
   if (wave < NB) {
-    const int b = wave;
-    uint64_t *ck = reinterpret_cast<uint64_t *>(kbuf) + b * 16;                 // [NB][16] keys
-    double *cv = reinterpret_cast<double *>(kbuf) + NB * 16 + b * 16;           // values
-    int *cid = reinterpret_cast<int *>(reinterpret_cast<double *>(kbuf) + 2 * NB * 16) + b * 16;   // ids
-    double v[kJ];
-#pragma unroll
-    for (int j = 0; j < kJ; ++j)   // clamped and unconditional: all loads in flight at once
-      v[j] = ld_dev(lg + b * kMaxExperts + min(lane + 64 * j, E - 1));
-    const float gam = ld_dev(gm + b);
-    uint64_t kk[kJ];
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) {
-      // + 0.0 folds -0 into +0 so that equal logits tie on the id alone;
-      // padding keys are 0, below every finite logit's key and below every
-      // prefix the select tries
-      const bool in = lane + 64 * j < E;
-      kk[j] = in ? order_key(v[j] + 0.0) : 0;
-    }
-    uint64_t T = 0;
-    int cnt = kJ * 64;   // keys >= T
-    for (int bit = 63; bit >= 0 && cnt != k; --bit) {
-      const uint64_t c = T | (uint64_t(1) << bit);
-      int n = 0;
-#pragma unroll
-      for (int j = 0; j < kJ; ++j) n += __popcll(__ballot(kk[j] >= c));
-      if (n >= k) {
-        T = c;
-        cnt = n;
-      }
-    }
-    int need = k;   // places left for keys equal to T
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) need -= __popcll(__ballot(kk[j] > T));
-    const uint64_t below = (uint64_t(1) << lane) - 1;
-    int eq_before = 0, packed = 0;
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) {
-      const bool eq = kk[j] == T;
-      const uint64_t eqm = __ballot(eq);
-      const bool take = kk[j] > T || (eq && eq_before + __popcll(eqm & below) < need);
-      const uint64_t tm = __ballot(take);
-      if (take) {
-        const int ci = packed + __popcll(tm & below);
-        ck[ci] = kk[j];
-        cv[ci] = v[j] + 0.0;
-        cid[ci] = lane + 64 * j;
-      }
-      eq_before += __popcll(eqm);
-      packed += __popcll(tm);
-    }
-    __builtin_amdgcn_wave_barrier();
-    // rank of packed entry `lane` (LDS accesses of one wave complete in
-    // order, so the wave reads back what its lanes wrote)
-    const bool me = lane < k;
-    const uint64_t mk = ck[me ? lane : 0];
-    const int mid = cid[me ? lane : 0];
-    const double mv = cv[me ? lane : 0];
-    int rank = 0;
-#pragma unroll
-    for (int q = 0; q < kMaxTopK; ++q)
-      if (q < k) rank += int(pair_before(ck[q], cid[q], mk, mid));
-    if (me) {
-      s.sel[b][rank] = mid;
-      s.selv[b][rank] = mv;
-    }
-    if (lane == 0) s.gam[b] = gam;
-    if (blockIdx.x == 0) {   // caller-visible logits (as published)
-#pragma unroll
-      for (int j = 0; j < kJ; ++j)
-        if (lane + 64 * j < E) a.l.logits[b * E + lane + 64 * j] = v[j];
-    }
+    if (a.l.n_experts <= 128) select_row<NB, 2>(a, s, lg, gm, kbuf, wave);
+    else select_row<NB, kMaxExperts / 64>(a, s, lg, gm, kbuf, wave);
   }
   __syncthreads();
 }
@@ -305,7 +315,11 @@ __device__ __forceinline__ void route_union(const LayerArgs &a, Shared<NB> &s, c
     __builtin_amdgcn_wave_barrier();
     // softmax of each row's k selected logits, summed in rank order
     double sum = 0.0;
-    for (int r = 0; r < k; ++r) sum += s.exq[lb * k + r];
+#pragma unroll
+    for (int r = 0; r < kMaxTopK; ++r) {   // every read issued at once; adding 0 past k
+      const double e = s.exq[min(lb * k + r, 63)];
+      sum += r < k ? e : 0.0;
+    }
     const float w_l = ent ? float(ex / sum) : 0.0f;
     if (ent) s.wsel[lb][lr] = w_l;
     if (lane == 0) s.u = u;
