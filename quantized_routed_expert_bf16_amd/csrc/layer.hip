@@ -52,6 +52,7 @@ constexpr int kStagePad = 4;                          // floats after each stage
 // staged act floats per row of x: (slot groups x kSlotBatch) runs of W + pad, W >= 32
 constexpr int kStageFloats = kStageCols * kSlotBatch + (kStageCols / kChunk) * kSlotBatch * kStagePad;
 constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr int kKeyFloats = 16 * (8 + 8 + 4) / 4;       // routing select scratch per row: keys, values, ids
 
 struct LayerArgs {
   LayerLaunch l;
@@ -507,6 +508,219 @@ __device__ __forceinline__ void run_gate_up(const LayerArgs &a, int x, uint64_t 
     __hip_atomic_fetch_add(sw(a, x, kSliceGu), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ------------------------------------------------- gate / up on MFMA
+// With two or more rows the dequantised dot products dominate the VALU time
+// of a gate/up unit (one FMA per code and row).  For 4-bit records (and
+// H <= 2048) the unit runs on v_mfma_f32_16x16x32_f16 instead: A = the 16
+// rows of the unit (8 gate/up pairs) as exact f16 integers, B = x split into
+// f16 high and low halves (columns b and 4 + b for row b), one 64-code group
+// (two MFMAs) per accumulator so that the group's scale and bias apply after
+// the product: y += s * (q . x) + b * sum(x).  Wave w takes the unit's 16
+// rows over groups [w G/4, (w+1) G/4); the waves' partial rows are summed in
+// LDS.
+//
+// Operand order.  Lane l holds A row l % 16 and B column l % 16 at k-slot
+// q = l / 16.  The four slot lanes of a row load 64 contiguous bytes, two
+// groups, with one 16-byte load each (slots 0, 1: halves of the even group,
+// slots 2, 3: of the odd one); swapping the upper two words between slots q
+// and q ^ 2 leaves every lane two words (16 codes) of each group: slot q of
+// group g holds codes base(g, q) + 8 st + (0..7) in step st, with base =
+// 16 (2 (q & 1) + ((q >> 1) ^ (g & 1))).  A word is expanded as code pairs
+// (0,4), (1,5), (2,6), (3,7).  The B fragments are staged once per block in
+// the same order.
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+template <int NB, int CPL>
+constexpr bool kMfmaGu = NB >= 2 && CPL == 1;
+
+constexpr int kMfmaHidden = 64 * kChunk;               // the one H the MFMA units take (2048)
+constexpr int kMG = kMfmaHidden / kGroup;               // groups per row (32)
+constexpr int kMGw = kMG / kWaves;                      // groups per wave (8)
+
+// x as MFMA B fragments: [group][step][slot][column 0..7] half8; and per
+// group the sums of x in columns 0..NB-1 (0 elsewhere).
+
+template <int NB>
+__device__ __forceinline__ void stage_x_fragments(const LayerArgs &a, const float *xs, const float *xsum,
+                                                  uint4 *xb, float *xg) {
+  constexpr int nch = kMfmaHidden / kChunk;
+  const ChunkX X0{reinterpret_cast<const float4 *>(xs), nch, 0};
+  for (int i = threadIdx.x; i < kMG * 64; i += kThreads) {
+    const int j = i & 7, q = (i >> 3) & 3, st = (i >> 5) & 1, g = i >> 6;
+    const int b = j & 3, part = j >> 2;
+    uint4 out = make_uint4(0, 0, 0, 0);
+    if (b < NB) {
+      // inputs k0 .. k0 + 7; the slot order alternates with the group's
+      // parity
+      const int k0 = kGroup * g + 16 * (2 * (q & 1) + ((q >> 1) ^ (g & 1))) + 8 * st;
+      const ChunkX X{X0.p, nch, k0 / kChunk};
+      const float4 f0 = X(b, (k0 % kChunk) / 4), f1 = X(b, (k0 % kChunk) / 4 + 1);
+      const float f[8] = {f0.x, f1.x, f0.y, f1.y, f0.z, f1.z, f0.w, f1.w};   // codes 0,4,1,5,2,6,3,7
+      uint32_t h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        half2v v;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const _Float16 hi = _Float16(f[2 * e + t]);
+          v[t] = part ? _Float16(f[2 * e + t] - float(hi)) : hi;
+        }
+        h[e] = __builtin_bit_cast(uint32_t, v);
+      }
+      out = make_uint4(h[0], h[1], h[2], h[3]);
+    }
+    xb[i] = out;
+  }
+  for (int i = threadIdx.x; i < kMG * 8; i += kThreads) {
+    const int j = i & 7, g = i >> 3;
+    xg[i] = j < NB ? xsum[j * nch + 2 * g] + xsum[j * nch + 2 * g + 1] : 0.0f;
+  }
+}
+
+// One 4-bit code word as an A fragment: f16 pairs (0,4), (1,5), (2,6), (3,7).
+// Nibbles at bits 0..3 of a half become 1024 + q and at bits 4..7 1024 + 16q
+// (exponent bits OR-ed in); one packed f16 add or fma takes them to q exactly.
+__device__ __forceinline__ half8 word_to_a(uint32_t w) {
+  const half2v k1024 = {_Float16(-1024.0f), _Float16(-1024.0f)};
+  const half2v s16 = {_Float16(0.0625f), _Float16(0.0625f)};
+  const half2v k64 = {_Float16(-64.0f), _Float16(-64.0f)};
+  const uint32_t t = w >> 8;
+  const half2v p0 = __builtin_bit_cast(half2v, (w & 0x000F000Fu) | 0x64006400u) + k1024;
+  const half2v p1 = __builtin_bit_cast(half2v, (w & 0x00F000F0u) | 0x64006400u) * s16 + k64;
+  const half2v p2 = __builtin_bit_cast(half2v, (t & 0x000F000Fu) | 0x64006400u) + k1024;
+  const half2v p3 = __builtin_bit_cast(half2v, (t & 0x00F000F0u) | 0x64006400u) * s16 + k64;
+  return half8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// The lane's code words and (scale, bias) words of a unit: row l % 16 of
+// the unit, slot l / 16, the wave's groups; (scale, bias) of that row for
+// the wave's groups 2 (l / 16) and 2 (l / 16) + 1.
+struct GuRegsM {
+  uint4 c[kMGw / 2];
+  uint2 s;
+};
+
+__device__ __forceinline__ void gate_up_load_m(const LayerArgs &a, uint64_t desc, int x, int unit, GuRegsM &r) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const RecordLayout L = record_layout(kMfmaHidden, a.l.inter, 4);
+  const uint8_t *rec = a.l.pool + (desc & ~uint64_t(255));
+  const int r0 = 2 * (x * a.W + unit * kTileRowPairs);   // the unit's first of 16 rows
+  const int q = lane >> 4, rr = r0 + (lane & 15);
+  const uint8_t *row = rec + L.gu_codes + size_t(rr) * L.gu_row_bytes + 32 * (wave * kMGw) + 16 * q;
+#pragma unroll
+  for (int gp = 0; gp < kMGw / 2; ++gp) r.c[gp] = *reinterpret_cast<const uint4 *>(row + 64 * gp);
+  const uint32_t *sb = reinterpret_cast<const uint32_t *>(rec + L.gu_sb);
+  r.s = *reinterpret_cast<const uint2 *>(sb + size_t(rr) * kMG + wave * kMGw + 2 * q);
+}
+
+// `red` holds one 512-byte slice per wave: first the wave's (scale, bias)
+// words [group][16 rows], then its partial rows [16 rows][8 columns].
+template <int NB>
+__device__ __forceinline__ void gate_up_unit_m(const LayerArgs &a, const GuRegsM &r, int x, int unit, int act_slot,
+                                               const uint4 *xb, const float *xg, float *red, uint32_t ep) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int I = a.l.inter;
+  const int q = lane >> 4, j = lane & 15;
+  float *slice = red + wave * 128;
+  uint32_t *sbl = reinterpret_cast<uint32_t *>(slice);
+  sbl[2 * q * 16 + j] = r.s.x;
+  sbl[(2 * q + 1) * 16 + j] = r.s.y;
+  __builtin_amdgcn_wave_barrier();
+  const int partner = (lane ^ 32) * 4;   // ds_bpermute address of slot q ^ 2
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  uint32_t ex0 = 0, ex1 = 0;
+  floatx4 tot = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int gi = 0; gi < kMGw; ++gi) {
+    const int g = wave * kMGw + gi;
+    // LDS operands first (columns 8..15 read columns 0..7 and are masked)
+    const float xsg0 = xg[g * 8 + (j & 7)];
+    const uint4 sv = *reinterpret_cast<const uint4 *>(sbl + gi * 16 + 4 * q);   // rows 4q .. 4q + 3
+    const uint4 b0 = xb[((g * 2 + 0) * 4 + q) * 8 + (j & 7)];
+    const uint4 b1 = xb[((g * 2 + 1) * 4 + q) * 8 + (j & 7)];
+    // the lane's two words of group g: its own lower pair for the group its
+    // slot loaded, the partner slot's upper pair for the other one
+    const uint4 v = r.c[gi / 2];
+    const bool own = ((q >> 1) == (gi & 1));
+    uint32_t w0 = v.x, w1 = v.y;
+    if ((gi & 1) == 0) {   // one exchange serves both groups of the pair
+      const uint32_t o0 = __builtin_amdgcn_ds_bpermute(partner, v.z);
+      const uint32_t o1 = __builtin_amdgcn_ds_bpermute(partner, v.w);
+      w0 = own ? v.x : o0;
+      w1 = own ? v.y : o1;
+      ex0 = o0;
+      ex1 = o1;
+    } else {
+      w0 = own ? v.x : ex0;
+      w1 = own ? v.y : ex1;
+    }
+    const half8 A0 = word_to_a(w0), A1 = word_to_a(w1);
+    const half8 B0 = __builtin_bit_cast(half8, j < 8 ? b0 : z);
+    const half8 B1 = __builtin_bit_cast(half8, j < 8 ? b1 : z);
+    floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, B0, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, B1, acc, 0, 0, 0);
+    const float xsg = j < 8 ? xsg0 : 0.0f;
+    const uint32_t sw4[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tot[i] = fmaf(sb_scale(sw4[i]), acc[i], fmaf(sb_bias(sw4[i]), xsg, tot[i]));
+  }
+  // partial rows 4q + i, column j of this wave -> its slice; then row pairs
+  __builtin_amdgcn_wave_barrier();
+  if (j < 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) slice[(4 * q + i) * 8 + j] = tot[i];
+  }
+  __syncthreads();
+  if (threadIdx.x < kTileRowPairs * NB) {
+    const int p = threadIdx.x / NB, b = threadIdx.x % NB;
+    float gs = 0.0f, us = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      gs += red[w * 128 + (2 * p) * 8 + b] + red[w * 128 + (2 * p) * 8 + 4 + b];
+      us += red[w * 128 + (2 * p + 1) * 8 + b] + red[w * 128 + (2 * p + 1) * 8 + 4 + b];
+    }
+    const int j0 = x * a.W + unit * kTileRowPairs;
+    st_dev(a.l.act + (size_t(act_slot) * kMaxNb + b) * I + j0 + p, tag_f32(ep, silu_mul(gs, us)));
+  }
+}
+
+template <int NB, bool kLoaded = false>
+__device__ __forceinline__ void run_gate_up_m(const LayerArgs &a, int x, uint64_t desc, int act_slot, int unit,
+                                              const uint4 *xb, const float *xg, float *red, uint32_t ep,
+                                              GuRegsM &r) {
+  if constexpr (!kLoaded) gate_up_load_m(a, desc, x, unit, r);
+  gate_up_unit_m<NB>(a, r, x, unit, act_slot, xb, xg, red, ep);
+  __syncthreads();   // every wave has issued its stores; red is free again
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(sw(a, x, kSliceGu), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Whether a unit of this record runs on MFMA.
+template <int NB, int CPL>
+__device__ __forceinline__ bool unit_on_mfma(const LayerArgs &a, uint64_t desc) {
+  if constexpr (kMfmaGu<NB, CPL>)
+    return a.l.hidden == kMfmaHidden && bits_of_tag(desc) == 4 &&
+           record_ok(desc, a.l.pool_bytes, a.l.hidden, a.l.inter);
+  return false;
+}
+
+// A gate/up unit on whichever path its record takes.
+template <int NB, int CPL>
+__device__ __forceinline__ void gate_up_item(const LayerArgs &a, int x, uint64_t desc, int act_slot, int unit,
+                                             const float *xs, const float *xsum, const uint4 *xb,
+                                             const float *xg, float *red, uint32_t ep) {
+  if (unit_on_mfma<NB, CPL>(a, desc)) {
+    GuRegsM r;
+    run_gate_up_m<NB>(a, x, desc, act_slot, unit, xb, xg, red, ep, r);
+  } else {
+    GuRegs<CPL> r;
+    run_gate_up<NB, CPL>(a, x, desc, act_slot, unit, xs, xsum, ep, r);
+  }
+}
+
 // ----------------------------------------------------------------- down
 // A down tile: 32 output rows of the slice's columns, every slot.  Lane
 // (row rw, chunk c, slot group g) of a wave handles row rw, 32-code chunk c
@@ -687,6 +901,11 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
   float *xs = reinterpret_cast<float *>(dyn);           // [NB][H]
   float *xsum = xs + NB * H;                            // [NB][H/32]
   float *keys = xsum + NB * (H / kChunk);               // routing build scratch
+  // MFMA gate/up operands after the keys: B fragments, group sums, the
+  // waves' partial rows
+  uint4 *xb = reinterpret_cast<uint4 *>(keys + kKeyFloats * NB);
+  float *xg = reinterpret_cast<float *>(xb) + (kMfmaGu<NB, CPL> ? kMG * 256 : 0);
+  float *red = xg + kMG * 8;
   float *act_lds = xs;                                  // [batch slots][NB][W + pad]
   float *asum_lds = act_lds + kStageFloats * NB;       // [batch slots][NB][W/32]
 
@@ -750,11 +969,15 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
         __hip_atomic_fetch_add(sw(a, threadIdx.x, kSliceRoute), 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
-    // the shared expert's gate/up units need no routing
-    for (int i = ((lr - R) % P + P) % P; i < a.ups; i += P) {
-      GuRegs<CPL> r;
-      run_gate_up<NB, CPL>(a, x, a.l.shared_rec, kSharedSlot, i, xs, xsum, sh.ep, r);
+    if constexpr (kMfmaGu<NB, CPL>) {   // after the router rows: they are on the routing path
+      if (H == kMfmaHidden) {
+        stage_x_fragments<NB>(a, xs, xsum, xb, xg);
+        __syncthreads();
+      }
     }
+    // the shared expert's gate/up units need no routing
+    for (int i = ((lr - R) % P + P) % P; i < a.ups; i += P)
+      gate_up_item<NB, CPL>(a, x, a.l.shared_rec, kSharedSlot, i, xs, xsum, xb, xg, red, sh.ep);
 
     wait_geq(a, sw(a, x, kSliceRoute), uint32_t(a.route_blocks));
     route_select<NB>(a, sh, lg, gm, reinterpret_cast<uint8_t *>(keys));
@@ -764,30 +987,39 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
     // already: its weights load while the union is built.
     int i = ((lr - R - a.ups) % P + P) % P;
     const int slot0 = i / a.ups;
-    GuRegs<CPL> pre;
     const bool early = slot0 < a.l.top_k;
     uint64_t d0 = 0;
     // retire every older vector memory access first, so that nothing in the
     // union build has to wait on these loads
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    if (early) {
-      d0 = rec_lds[sh.sel[0][slot0]];
-      if (record_ok(d0, a.l.pool_bytes, a.l.hidden, a.l.inter))
+    if (early) d0 = rec_lds[sh.sel[0][slot0]];
+    if constexpr (kMfmaGu<NB, CPL>) {
+      GuRegsM pre;
+      const bool em = early && unit_on_mfma<NB, CPL>(a, d0);
+      if (em) gate_up_load_m(a, d0, x, i - slot0 * a.ups, pre);
+      asm volatile("" ::: "memory");   // the loads are issued here, not sunk to their use
+      route_union<NB>(a, sh, rec_lds);
+      if (em) {   // slot0 < k <= u: a gate/up unit
+        run_gate_up_m<NB, true>(a, x, d0, slot0, i - slot0 * a.ups, xb, xg, red, sh.ep, pre);
+        i += P;
+      }
+    } else {
+      GuRegs<CPL> pre;
+      if (early && record_ok(d0, a.l.pool_bytes, a.l.hidden, a.l.inter))
         gate_up_load_any<CPL>(a, d0, gate_up_row0(a, x, i - slot0 * a.ups), pre);
+      asm volatile("" ::: "memory");   // the loads are issued here, not sunk to their use
+      route_union<NB>(a, sh, rec_lds);
+      if (early) {   // slot0 < k <= u: a gate/up unit
+        run_gate_up<NB, CPL, true>(a, x, d0, slot0, i - slot0 * a.ups, xs, xsum, sh.ep, pre);
+        i += P;
+      }
     }
-    asm volatile("" ::: "memory");   // the loads are issued here, not sunk to their use
-    route_union<NB>(a, sh, rec_lds);
     const int u = sh.u;
     const int n_gu = u * a.ups;
     const int n_total = n_gu + a.tiles;
-    if (early) {   // slot0 < k <= u: a gate/up unit
-      run_gate_up<NB, CPL, true>(a, x, d0, slot0, i - slot0 * a.ups, xs, xsum, sh.ep, pre);
-      i += P;
-    }
     for (; i < n_gu; i += P) {
       const int slot = i / a.ups;
-      GuRegs<CPL> r;
-      run_gate_up<NB, CPL>(a, x, sh.desc[slot], slot, i - slot * a.ups, xs, xsum, sh.ep, r);
+      gate_up_item<NB, CPL>(a, x, sh.desc[slot], slot, i - slot * a.ups, xs, xsum, xb, xg, red, sh.ep);
     }
     for (; i < n_total; i += P) run_down<NB>(a, sh, x, i - n_gu, act_lds, asum_lds);
   }
@@ -806,10 +1038,13 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
 }
 
 size_t dyn_lds_bytes(int nb, int hidden) {
-  // x, its per-32 sums and the logit keys; or one batch of staged act chunks
-  // and their sums
+  // x, its per-32 sums and the logit keys (and with MFMA gate/up units the B
+  // fragments, group sums and partial rows); or one batch of staged act
+  // chunks and their sums
+  const bool mfma = nb >= 2 && hidden == kMfmaHidden;
   const size_t xk = sizeof(float) * (size_t(nb) * hidden + size_t(nb) * (hidden / kChunk)) +
-                    size_t(nb) * kMaxExperts * (8 + 8 + 4 + 4 + 4);
+                    sizeof(float) * kKeyFloats * nb +
+                    (mfma ? size_t(kMG) * (1024 + 32) + sizeof(float) * kWaves * 128 : 0);
   const size_t st = sizeof(float) * (size_t(kStageFloats) * nb + size_t(8) * kSlotBatch * nb);
   return xk > st ? xk : st;
 }
