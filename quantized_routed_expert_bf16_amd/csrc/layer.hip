@@ -532,8 +532,6 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
-template <int NB, int CPL>
-constexpr bool kMfmaGu = NB >= 2 && CPL == 1;
 
 constexpr int kMfmaHidden = 64 * kChunk;               // the one H the MFMA units take (2048)
 constexpr int kMG = kMfmaHidden / kGroup;               // groups per row (32)
@@ -594,6 +592,36 @@ __device__ __forceinline__ half8 word_to_a(uint32_t w) {
   return half8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// A 2- or 3-bit code word (16 codes) as two A fragments in the same k
+// order as word_to_a gives a 4-bit word's codes: step 0 holds codes 0..7 as
+// pairs (0,4), (1,5), (2,6), (3,7), step 1 codes 8..15 likewise.  One byte
+// permute puts byte 1 (codes 4..7) beside byte 0 in the other half word;
+// field p of a byte, scaled by 4^p once in place, is undone by one packed
+// f16 fma.  `hb`: the high bits of the word's codes, bit 8k + p for code
+// 4k + p (3-bit only).
+template <int BITS>
+__device__ __forceinline__ void lowbit_to_a(uint32_t w, uint32_t hb, half8 &A0, half8 &A1) {
+  const uint32_t wp = __builtin_amdgcn_perm(0u, w, 0x03010200u);
+  const uint32_t hp = BITS == 3 ? __builtin_amdgcn_perm(0u, hb, 0x03010200u) : 0u;
+  half8 A[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const uint32_t x = wp >> (8 * st), xh = hp >> (8 * st);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t v = (x & (0x00030003u << (2 * p))) | 0x64006400u;
+      if constexpr (BITS == 3) v |= (xh & (0x00010001u << p)) << (p + 2);
+      const float sc = 1.0f / float(1 << (2 * p));
+      const half2v m = {_Float16(sc), _Float16(sc)}, o = {_Float16(-1024.0f * sc), _Float16(-1024.0f * sc)};
+      const half2v h = __builtin_bit_cast(half2v, v) * m + o;
+      A[st][2 * p] = h[0];
+      A[st][2 * p + 1] = h[1];
+    }
+  }
+  A0 = A[0];
+  A1 = A[1];
+}
+
 // The lane's code words and (scale, bias) words of a unit: row l % 16 of
 // the unit, slot l / 16, the wave's groups; (scale, bias) of that row for
 // the wave's groups 2 (l / 16) and 2 (l / 16) + 1.
@@ -602,24 +630,56 @@ struct GuRegsM {
   uint2 s;
 };
 
+// 4-bit: c[gp] = the row's 16 bytes of group pair gp in the lane's slot.
+// 2/3-bit: coalesced row pieces, rearranged through LDS by the unit:
+// c[0], c[1] = low-plane bytes 16 (l % 8) .. + 15 (group l % 8 of the wave)
+// of rows l / 8 and 8 + l / 8; c[2] = high-plane bytes 16 (l % 4) .. + 15
+// (chunks 4 (l % 4) .. + 3 of the wave) of row l / 4.
+template <int BITS>
 __device__ __forceinline__ void gate_up_load_m(const LayerArgs &a, uint64_t desc, int x, int unit, GuRegsM &r) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const RecordLayout L = record_layout(kMfmaHidden, a.l.inter, 4);
+  const RecordLayout L = record_layout(kMfmaHidden, a.l.inter, BITS);
   const uint8_t *rec = a.l.pool + (desc & ~uint64_t(255));
   const int r0 = 2 * (x * a.W + unit * kTileRowPairs);   // the unit's first of 16 rows
   const int q = lane >> 4, rr = r0 + (lane & 15);
-  const uint8_t *row = rec + L.gu_codes + size_t(rr) * L.gu_row_bytes + 32 * (wave * kMGw) + 16 * q;
+  const uint8_t *codes = rec + L.gu_codes;
+  if constexpr (BITS == 4) {
+    const uint8_t *row = codes + size_t(rr) * L.gu_row_bytes + 32 * (wave * kMGw) + 16 * q;
 #pragma unroll
-  for (int gp = 0; gp < kMGw / 2; ++gp) r.c[gp] = *reinterpret_cast<const uint4 *>(row + 64 * gp);
+    for (int gp = 0; gp < kMGw / 2; ++gp) r.c[gp] = *reinterpret_cast<const uint4 *>(row + 64 * gp);
+  } else {
+    const int lo = kMGw * kGroup / 4;   // low-plane bytes of the wave's groups per row (128)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      r.c[h] = *reinterpret_cast<const uint4 *>(codes + size_t(r0 + (lane >> 3) + 8 * h) * L.gu_row_bytes +
+                                                lo * wave + 16 * (lane & 7));
+    if constexpr (BITS == 3)
+      r.c[2] = *reinterpret_cast<const uint4 *>(codes + size_t(r0 + (lane >> 2)) * L.gu_row_bytes +
+                                                kMfmaHidden / 4 + (lo / 2) * wave + 16 * (lane & 3));
+  }
   const uint32_t *sb = reinterpret_cast<const uint32_t *>(rec + L.gu_sb);
   r.s = *reinterpret_cast<const uint2 *>(sb + size_t(rr) * kMG + wave * kMGw + 2 * q);
 }
 
+__device__ __forceinline__ void gate_up_load_m_any(const LayerArgs &a, uint64_t desc, int x, int unit, GuRegsM &r) {
+  switch (bits_of_tag(desc)) {
+    case 4: gate_up_load_m<4>(a, desc, x, unit, r); break;
+    case 3: gate_up_load_m<3>(a, desc, x, unit, r); break;
+    default: gate_up_load_m<2>(a, desc, x, unit, r); break;
+  }
+}
+
+// Per-wave LDS rows for 2/3-bit codes: [16 rows][kLbRow words]: 32 low-plane
+// words (group-major, 4 per group), then 16 high-plane words (one per chunk).
+constexpr int kLbRow = 52;
+constexpr int kLbWave = 16 * kLbRow;
+
 // `red` holds one 512-byte slice per wave: first the wave's (scale, bias)
 // words [group][16 rows], then its partial rows [16 rows][8 columns].
-template <int NB>
+template <int NB, int BITS>
 __device__ __forceinline__ void gate_up_unit_m(const LayerArgs &a, const GuRegsM &r, int x, int unit, int act_slot,
-                                               const uint4 *xb, const float *xg, float *red, uint32_t ep) {
+                                               const uint4 *xb, const float *xg, float *red, uint32_t *stg,
+                                               uint32_t ep) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int I = a.l.inter;
   const int q = lane >> 4, j = lane & 15;
@@ -627,6 +687,13 @@ __device__ __forceinline__ void gate_up_unit_m(const LayerArgs &a, const GuRegsM
   uint32_t *sbl = reinterpret_cast<uint32_t *>(slice);
   sbl[2 * q * 16 + j] = r.s.x;
   sbl[(2 * q + 1) * 16 + j] = r.s.y;
+  uint32_t *lb = stg + wave * kLbWave;
+  if constexpr (BITS != 4) {   // the wave's rows into LDS, read back in slot order below
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      *reinterpret_cast<uint4 *>(lb + ((lane >> 3) + 8 * h) * kLbRow + 4 * (lane & 7)) = r.c[h];
+    if constexpr (BITS == 3) *reinterpret_cast<uint4 *>(lb + (lane >> 2) * kLbRow + 32 + 4 * (lane & 3)) = r.c[2];
+  }
   __builtin_amdgcn_wave_barrier();
   const int partner = (lane ^ 32) * 4;   // ds_bpermute address of slot q ^ 2
   const uint4 z = make_uint4(0, 0, 0, 0);
@@ -640,23 +707,37 @@ __device__ __forceinline__ void gate_up_unit_m(const LayerArgs &a, const GuRegsM
     const uint4 sv = *reinterpret_cast<const uint4 *>(sbl + gi * 16 + 4 * q);   // rows 4q .. 4q + 3
     const uint4 b0 = xb[((g * 2 + 0) * 4 + q) * 8 + (j & 7)];
     const uint4 b1 = xb[((g * 2 + 1) * 4 + q) * 8 + (j & 7)];
-    // the lane's two words of group g: its own lower pair for the group its
-    // slot loaded, the partner slot's upper pair for the other one
-    const uint4 v = r.c[gi / 2];
-    const bool own = ((q >> 1) == (gi & 1));
-    uint32_t w0 = v.x, w1 = v.y;
-    if ((gi & 1) == 0) {   // one exchange serves both groups of the pair
-      const uint32_t o0 = __builtin_amdgcn_ds_bpermute(partner, v.z);
-      const uint32_t o1 = __builtin_amdgcn_ds_bpermute(partner, v.w);
-      w0 = own ? v.x : o0;
-      w1 = own ? v.y : o1;
-      ex0 = o0;
-      ex1 = o1;
+    half8 A0, A1;
+    if constexpr (BITS == 4) {
+      // the lane's two words of group g: its own lower pair for the group
+      // its slot loaded, the partner slot's upper pair for the other one
+      const uint4 v = r.c[gi / 2];
+      const bool own = ((q >> 1) == (gi & 1));
+      uint32_t w0 = v.x, w1 = v.y;
+      if ((gi & 1) == 0) {   // one exchange serves both groups of the pair
+        const uint32_t o0 = __builtin_amdgcn_ds_bpermute(partner, v.z);
+        const uint32_t o1 = __builtin_amdgcn_ds_bpermute(partner, v.w);
+        w0 = own ? v.x : o0;
+        w1 = own ? v.y : o1;
+        ex0 = o0;
+        ex1 = o1;
+      } else {
+        w0 = own ? v.x : ex0;
+        w1 = own ? v.y : ex1;
+      }
+      A0 = word_to_a(w0);
+      A1 = word_to_a(w1);
     } else {
-      w0 = own ? v.x : ex0;
-      w1 = own ? v.y : ex1;
+      // the slot's word of the group (codes 16 wq .. + 15) and, 3-bit, the
+      // high bits of those codes: nibble wq % 2 of each byte of the high
+      // word of chunk 2 gi + wq / 2
+      const int wq = 2 * (q & 1) + ((q >> 1) ^ (gi & 1));
+      const uint32_t *rowp = lb + (lane & 15) * kLbRow;
+      const uint32_t w = rowp[4 * gi + wq];
+      uint32_t hb = 0;
+      if constexpr (BITS == 3) hb = (rowp[32 + 2 * gi + (wq >> 1)] >> (4 * (wq & 1))) & 0x0F0F0F0Fu;
+      lowbit_to_a<BITS>(w, hb, A0, A1);
     }
-    const half8 A0 = word_to_a(w0), A1 = word_to_a(w1);
     const half8 B0 = __builtin_bit_cast(half8, j < 8 ? b0 : z);
     const half8 B1 = __builtin_bit_cast(half8, j < 8 ? b1 : z);
     floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -687,34 +768,55 @@ __device__ __forceinline__ void gate_up_unit_m(const LayerArgs &a, const GuRegsM
   }
 }
 
-template <int NB, bool kLoaded = false>
-__device__ __forceinline__ void run_gate_up_m(const LayerArgs &a, int x, uint64_t desc, int act_slot, int unit,
-                                              const uint4 *xb, const float *xg, float *red, uint32_t ep,
-                                              GuRegsM &r) {
-  if constexpr (!kLoaded) gate_up_load_m(a, desc, x, unit, r);
-  gate_up_unit_m<NB>(a, r, x, unit, act_slot, xb, xg, red, ep);
+// The unit's act stores are issued by every wave: count it for the slice.
+__device__ __forceinline__ void gate_up_signal(const LayerArgs &a, int x) {
   __syncthreads();   // every wave has issued its stores; red is free again
   if (threadIdx.x == 0)
     __hip_atomic_fetch_add(sw(a, x, kSliceGu), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Whether a unit of this record runs on MFMA.
-template <int NB, int CPL>
-__device__ __forceinline__ bool unit_on_mfma(const LayerArgs &a, uint64_t desc) {
-  if constexpr (kMfmaGu<NB, CPL>)
-    return a.l.hidden == kMfmaHidden && bits_of_tag(desc) == 4 &&
-           record_ok(desc, a.l.pool_bytes, a.l.hidden, a.l.inter);
-  return false;
+template <int NB, bool kLoaded = false>
+__device__ __forceinline__ void run_gate_up_m(const LayerArgs &a, int x, uint64_t desc, int act_slot, int unit,
+                                              const uint4 *xb, const float *xg, float *red, uint32_t *stg,
+                                              uint32_t ep, GuRegsM &r) {
+  if constexpr (!kLoaded) gate_up_load_m_any(a, desc, x, unit, r);
+  switch (bits_of_tag(desc)) {
+    case 4: gate_up_unit_m<NB, 4>(a, r, x, unit, act_slot, xb, xg, red, stg, ep); break;
+    case 3: gate_up_unit_m<NB, 3>(a, r, x, unit, act_slot, xb, xg, red, stg, ep); break;
+    default: gate_up_unit_m<NB, 2>(a, r, x, unit, act_slot, xb, xg, red, stg, ep); break;
+  }
+  gate_up_signal(a, x);
 }
 
-// A gate/up unit on whichever path its record takes.
-template <int NB, int CPL>
+// A unit whose descriptor fails the record check: its act values are 0
+// (status bit 0 tells the caller).
+template <int NB>
+__device__ __forceinline__ void gate_up_bad(const LayerArgs &a, int x, int act_slot, int unit, uint32_t ep) {
+  const int lane = threadIdx.x & 63;
+  const int j0 = gate_up_row0(a, x, unit);
+  if (threadIdx.x == 0) set_status(a, 1u);
+  if (lane < NB * kPairsPerWave)
+    st_dev(a.l.act + (size_t(act_slot) * kMaxNb + lane / kPairsPerWave) * a.l.inter + j0 + lane % kPairsPerWave,
+           tag_f32(ep, 0.0f));
+  gate_up_signal(a, x);
+}
+
+// A gate/up unit on the kernel's path: kM kernels (two to four rows,
+// H = 2048) run every unit on MFMA, the others on the VALU.
+template <int NB, int CPL, bool kM>
 __device__ __forceinline__ void gate_up_item(const LayerArgs &a, int x, uint64_t desc, int act_slot, int unit,
                                              const float *xs, const float *xsum, const uint4 *xb,
                                              const float *xg, float *red, uint32_t ep) {
-  if (unit_on_mfma<NB, CPL>(a, desc)) {
-    GuRegsM r;
-    run_gate_up_m<NB>(a, x, desc, act_slot, unit, xb, xg, red, ep, r);
+  if constexpr (kM) {
+    if (record_ok(desc, a.l.pool_bytes, a.l.hidden, a.l.inter)) {
+      GuRegsM r;
+      // x in f32 is dead once the B fragments are staged: its LDS takes the
+      // 2/3-bit code rows
+      run_gate_up_m<NB>(a, x, desc, act_slot, unit, xb, xg, red,
+                        reinterpret_cast<uint32_t *>(const_cast<float *>(xs)), ep, r);
+    } else {
+      gate_up_bad<NB>(a, x, act_slot, unit, ep);
+    }
   } else {
     GuRegs<CPL> r;
     run_gate_up<NB, CPL>(a, x, desc, act_slot, unit, xs, xsum, ep, r);
@@ -888,7 +990,7 @@ __device__ __forceinline__ void run_down(const LayerArgs &a, Shared<NB> &sh, int
 }
 
 // ---------------------------------------------------------------- kernel
-template <int NB, int CPL>
+template <int NB, int CPL, bool kM>
 __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
   extern __shared__ float4 dyn[];
   __shared__ Shared<NB> sh;
@@ -904,7 +1006,7 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
   // MFMA gate/up operands after the keys: B fragments, group sums, the
   // waves' partial rows
   uint4 *xb = reinterpret_cast<uint4 *>(keys + kKeyFloats * NB);
-  float *xg = reinterpret_cast<float *>(xb) + (kMfmaGu<NB, CPL> ? kMG * 256 : 0);
+  float *xg = reinterpret_cast<float *>(xb) + (kM ? kMG * 256 : 0);
   float *red = xg + kMG * 8;
   float *act_lds = xs;                                  // [batch slots][NB][W + pad]
   float *asum_lds = act_lds + kStageFloats * NB;       // [batch slots][NB][W/32]
@@ -969,15 +1071,13 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
         __hip_atomic_fetch_add(sw(a, threadIdx.x, kSliceRoute), 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
-    if constexpr (kMfmaGu<NB, CPL>) {   // after the router rows: they are on the routing path
-      if (H == kMfmaHidden) {
-        stage_x_fragments<NB>(a, xs, xsum, xb, xg);
-        __syncthreads();
-      }
+    if constexpr (kM) {   // after the router rows: they are on the routing path
+      stage_x_fragments<NB>(a, xs, xsum, xb, xg);
+      __syncthreads();
     }
     // the shared expert's gate/up units need no routing
     for (int i = ((lr - R) % P + P) % P; i < a.ups; i += P)
-      gate_up_item<NB, CPL>(a, x, a.l.shared_rec, kSharedSlot, i, xs, xsum, xb, xg, red, sh.ep);
+      gate_up_item<NB, CPL, kM>(a, x, a.l.shared_rec, kSharedSlot, i, xs, xsum, xb, xg, red, sh.ep);
 
     wait_geq(a, sw(a, x, kSliceRoute), uint32_t(a.route_blocks));
     route_select<NB>(a, sh, lg, gm, reinterpret_cast<uint8_t *>(keys));
@@ -993,14 +1093,18 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
     // union build has to wait on these loads
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     if (early) d0 = rec_lds[sh.sel[0][slot0]];
-    if constexpr (kMfmaGu<NB, CPL>) {
+    if constexpr (kM) {
       GuRegsM pre;
-      const bool em = early && unit_on_mfma<NB, CPL>(a, d0);
-      if (em) gate_up_load_m(a, d0, x, i - slot0 * a.ups, pre);
+      // (4-bit records only: the early loads stay out of the other widths'
+      // register budget)
+      const bool em = early && bits_of_tag(d0) == 4 && record_ok(d0, a.l.pool_bytes, a.l.hidden, a.l.inter);
+      if (em) gate_up_load_m<4>(a, d0, x, i - slot0 * a.ups, pre);
       asm volatile("" ::: "memory");   // the loads are issued here, not sunk to their use
       route_union<NB>(a, sh, rec_lds);
       if (em) {   // slot0 < k <= u: a gate/up unit
-        run_gate_up_m<NB, true>(a, x, d0, slot0, i - slot0 * a.ups, xb, xg, red, sh.ep, pre);
+        gate_up_unit_m<NB, 4>(a, pre, x, i - slot0 * a.ups, slot0, xb, xg, red, reinterpret_cast<uint32_t *>(xs),
+                              sh.ep);
+        gate_up_signal(a, x);
         i += P;
       }
     } else {
@@ -1019,7 +1123,7 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
     const int n_total = n_gu + a.tiles;
     for (; i < n_gu; i += P) {
       const int slot = i / a.ups;
-      gate_up_item<NB, CPL>(a, x, sh.desc[slot], slot, i - slot * a.ups, xs, xsum, xb, xg, red, sh.ep);
+      gate_up_item<NB, CPL, kM>(a, x, sh.desc[slot], slot, i - slot * a.ups, xs, xsum, xb, xg, red, sh.ep);
     }
     for (; i < n_total; i += P) run_down<NB>(a, sh, x, i - n_gu, act_lds, asum_lds);
   }
@@ -1037,11 +1141,10 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
   }
 }
 
-size_t dyn_lds_bytes(int nb, int hidden) {
+size_t dyn_lds_bytes(int nb, int hidden, bool mfma) {
   // x, its per-32 sums and the logit keys (and with MFMA gate/up units the B
   // fragments, group sums and partial rows); or one batch of staged act
   // chunks and their sums
-  const bool mfma = nb >= 2 && hidden == kMfmaHidden;
   const size_t xk = sizeof(float) * (size_t(nb) * hidden + size_t(nb) * (hidden / kChunk)) +
                     sizeof(float) * kKeyFloats * nb +
                     (mfma ? size_t(kMG) * (1024 + 32) + sizeof(float) * kWaves * 128 : 0);
@@ -1051,14 +1154,14 @@ size_t dyn_lds_bytes(int nb, int hidden) {
 
 struct LaunchCache {
   int device = -1;
-  int blocks_per_cu[kMaxNb + 1][3] = {};
+  int blocks_per_cu[kMaxNb + 1][3][2] = {};
   int cus = 0;
 };
 thread_local LaunchCache g_cache;
 
-template <int NB, int CPL>
+template <int NB, int CPL, bool kM>
 hipError_t launch_nb(LayerArgs &a, hipStream_t s) {
-  const size_t lds = dyn_lds_bytes(NB, a.l.hidden);
+  const size_t lds = dyn_lds_bytes(NB, a.l.hidden, kM);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -1068,10 +1171,10 @@ hipError_t launch_nb(LayerArgs &a, hipStream_t s) {
     e = hipDeviceGetAttribute(&g_cache.cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
   }
-  int &per_cu = g_cache.blocks_per_cu[NB][CPL];
+  int &per_cu = g_cache.blocks_per_cu[NB][CPL][kM];
   if (per_cu == 0) {
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, layer_kernel<NB, CPL>, kThreads,
-                                                     dyn_lds_bytes(NB, CPL * 64 * kChunk));
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, layer_kernel<NB, CPL, kM>, kThreads,
+                                                     dyn_lds_bytes(NB, CPL * 64 * kChunk, kM));
     if (e != hipSuccess) return e;
     if (per_cu < 1) return hipErrorInvalidConfiguration;
     if (per_cu > 2) per_cu = 2;
@@ -1079,7 +1182,7 @@ hipError_t launch_nb(LayerArgs &a, hipStream_t s) {
   const int grid = (per_cu * g_cache.cus) / kSlices * kSlices;
   a.per_slice = grid / kSlices;
   a.route_blocks = min(a.per_slice * a.n_slices, (a.l.n_experts + 1 + kWaves - 1) / kWaves);
-  hipLaunchKernelGGL((layer_kernel<NB, CPL>), dim3(grid), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((layer_kernel<NB, CPL, kM>), dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -1094,11 +1197,12 @@ hipError_t launch_layer(const LayerLaunch &l, hipStream_t s) {
   a.tiles = l.hidden / kRowsPerTile;
   if (a.tiles > kMaxDownTiles || a.W / kChunk > 8 || a.W % kTileRowPairs) return hipErrorInvalidValue;
   const bool two = l.hidden > 64 * kChunk;
+  const bool mfma = l.hidden == kMfmaHidden;   // gate/up units on MFMA for two to four rows
   switch (l.nb) {
-    case 1: return two ? launch_nb<1, 2>(a, s) : launch_nb<1, 1>(a, s);
-    case 2: return two ? launch_nb<2, 2>(a, s) : launch_nb<2, 1>(a, s);
-    case 3: return two ? launch_nb<3, 2>(a, s) : launch_nb<3, 1>(a, s);
-    default: return two ? launch_nb<4, 2>(a, s) : launch_nb<4, 1>(a, s);
+    case 1: return two ? launch_nb<1, 2, false>(a, s) : launch_nb<1, 1, false>(a, s);
+    case 2: return two ? launch_nb<2, 2, false>(a, s) : mfma ? launch_nb<2, 1, true>(a, s) : launch_nb<2, 1, false>(a, s);
+    case 3: return two ? launch_nb<3, 2, false>(a, s) : mfma ? launch_nb<3, 1, true>(a, s) : launch_nb<3, 1, false>(a, s);
+    default: return two ? launch_nb<4, 2, false>(a, s) : mfma ? launch_nb<4, 1, true>(a, s) : launch_nb<4, 1, false>(a, s);
   }
 }
 
