@@ -824,6 +824,46 @@ __device__ __forceinline__ void gate_up_item(const LayerArgs &a, int x, uint64_t
 }
 
 // ----------------------------------------------------------------- down
+// The block of slice tile % slices sums the tile's rows of every slice's
+// partial in slice order (re-reading, boundedly, partials not yet of this
+// call) into `out`.
+template <int NB>
+__device__ __forceinline__ void combine_tile(const LayerArgs &a, const Shared<NB> &sh, int x, int tile) {
+  const int H = a.l.hidden;
+  if (tile % a.n_slices == x) {   // this slice's block combines the tile's rows in slice order
+    for (int i = threadIdx.x; i < kRowsPerTile * NB; i += kThreads) {
+      const int b = i / kRowsPerTile, r = tile * kRowsPerTile + i % kRowsPerTile;
+      uint64_t w[kSlices];
+#pragma unroll
+      for (int q = 0; q < kSlices; ++q)
+        w[q] = q < a.n_slices ? ld_dev(a.l.opart + (size_t(q) * kMaxNb + b) * H + r) : 0;
+      for (uint32_t it = 1;; ++it) {   // re-read the partials not yet of this call (bounded)
+        bool all = true;
+#pragma unroll
+        for (int q = 0; q < kSlices; ++q) all &= q >= a.n_slices || uint32_t(w[q] >> 32) == sh.ep;
+        if (all) break;
+        if ((it & 63) == 0 && (ld_dev(a.l.sync + kSyncAbort) || it > kSpinLimit)) {
+          st_dev(a.l.sync + kSyncAbort, 1u);
+          set_status(a, 4u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+        for (int q = 0; q < kSlices; ++q)
+          if (q < a.n_slices && uint32_t(w[q] >> 32) != sh.ep)
+            w[q] = ld_dev(a.l.opart + (size_t(q) * kMaxNb + b) * H + r);
+      }
+      float v = 0.0f;
+#pragma unroll
+      for (int q = 0; q < kSlices; ++q)
+        if (q < a.n_slices) v += __uint_as_float(uint32_t(w[q]));
+      a.l.out[size_t(b) * H + r] = v;
+    }
+  }
+  __syncthreads();
+}
+
+
 // A down tile: 32 output rows of the slice's columns, every slot.  Lane
 // (row rw, chunk c, slot group g) of a wave handles row rw, 32-code chunk c
 // of the slice, and slots g, g + SG, ...; weights for the lane's slots are
@@ -956,18 +996,74 @@ __device__ __forceinline__ void run_down(const LayerArgs &a, Shared<NB> &sh, int
       st_dev(a.l.opart + (size_t(x) * kMaxNb + b) * H + row,
              (uint64_t(sh.ep) << 32) | __float_as_uint(acc[b]));
 
-  if (tile % a.n_slices == x) {   // this slice's block combines the tile's rows in slice order
-    for (int i = threadIdx.x; i < kRowsPerTile * NB; i += kThreads) {
-      const int b = i / kRowsPerTile, r = tile * kRowsPerTile + i % kRowsPerTile;
-      uint64_t w[kSlices];
+  combine_tile<NB>(a, sh, x, tile);
+}
+
+// ------------------------------------------------------- down on MFMA
+// In the MFMA kernels (W = 64: the slice's columns are one group of every
+// down row) a down tile runs as MFMAs too.  A = 16 down rows x the slot's 64
+// codes (the slot lane q holds codes 16q .. 16q + 15: step st takes codes
+// 16q + 8st + (0,4,1,5,2,6,3,7), the order of the gate/up units), B = act
+// of the slot as f16 high/low halves, staged per batch of slots straight
+// into that fragment order.  Wave w takes row block w % 2 of the tile and
+// the slots of parity w / 2; the two waves of a row block are summed in LDS.
+constexpr int kDownSlots = 8;   // slots per wave per batch (2 kDownSlots per block)
+
+template <int NB>
+__device__ __forceinline__ void run_down_m(const LayerArgs &a, Shared<NB> &sh, int x, int tile, uint4 *frag,
+                                           float *gsum, float *red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int H = a.l.hidden, I = a.l.inter;
+  const int q = lane >> 4, j = lane & 15;
+  const int rb = wave & 1, par = wave >> 1;
+  const int r0 = tile * kRowsPerTile + 16 * rb;   // the wave's 16 rows
+  const int u = sh.u, n_slots = u + 1;
+  floatx4 tot = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s0 = 0; s0 < n_slots; s0 += 2 * kDownSlots) {
+    // 1. the lane's code words and the (scale, bias) words of its 4 output
+    //    rows for the wave's slots of the batch
+    uint2 cw[kDownSlots];
+    uint4 sbv[kDownSlots];
 #pragma unroll
-      for (int q = 0; q < kSlices; ++q)
-        w[q] = q < a.n_slices ? ld_dev(a.l.opart + (size_t(q) * kMaxNb + b) * H + r) : 0;
-      for (uint32_t it = 1;; ++it) {   // re-read the partials not yet of this call (bounded)
-        bool all = true;
+    for (int m = 0; m < kDownSlots; ++m) {
+      const int slot = s0 + par + 2 * m;
+      const int bt = slot < n_slots ? sh.dbits[slot] : 0;
+      cw[m] = make_uint2(0, 0);
+      sbv[m] = make_uint4(0, 0, 0, 0);
+      if (bt) {
+        const uint8_t *grow = sh.dcodes[slot] + (size_t(x) * H + r0 + (lane & 15)) * (kGroup * bt / 8);
+        if (bt == 4) {
+          cw[m] = *reinterpret_cast<const uint2 *>(grow + 8 * q);
+        } else {
+          cw[m].x = *reinterpret_cast<const uint32_t *>(grow + 4 * q);
+          if (bt == 3) cw[m].y = *reinterpret_cast<const uint32_t *>(grow + 16 + 4 * (q >> 1));
+        }
+        sbv[m] = *reinterpret_cast<const uint4 *>(sh.dsb[slot] + size_t(x) * H + r0 + 4 * q);
+      }
+    }
+    // 2. the slice's act values must be complete
+    if (s0 == 0) wait_geq(a, sw(a, x, kSliceGu), uint32_t(n_slots * a.ups));
+    // 3. stage the batch's act as B fragments: item = (slot, row b, block
+    //    of 8 columns); one device-coherent pass of 8 tagged values each,
+    //    high and low halves in fragment order, and the slot's column sums
+    const int nbs = min(n_slots - s0, 2 * kDownSlots);
+    const int n_items = nbs * NB * 8;
+    __syncthreads();
+    for (int i0 = 0; i0 < n_items; i0 += kThreads) {   // every lane runs the DPP sum
+      const int i = i0 + threadIdx.x;
+      const int ic = min(i, n_items - 1);
+      const int blk = ic & 7, b = (ic >> 3) % NB, sl = (ic >> 3) / NB;
+      const int slot = s0 + sl;
+      const int ps = slot < u ? slot : kSharedSlot;
+      const uint32_t off = uint32_t(((ps * kMaxNb + b) * I + x * kGroup + 8 * blk) * 8);
+      uint64_t v[8];
 #pragma unroll
-        for (int q = 0; q < kSlices; ++q) all &= q >= a.n_slices || uint32_t(w[q] >> 32) == sh.ep;
-        if (all) break;
+      for (int t = 0; t < 4; ++t) ld_dev_u64x2(a.l.act, off + 16 * t, v[2 * t], v[2 * t + 1]);
+      for (uint32_t it = 1;; ++it) {   // values of an earlier call are read again (bounded)
+        bool stale = false;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) stale |= uint32_t(v[e] >> 32) != sh.ep;
+        if (!stale) break;
         if ((it & 63) == 0 && (ld_dev(a.l.sync + kSyncAbort) || it > kSpinLimit)) {
           st_dev(a.l.sync + kSyncAbort, 1u);
           set_status(a, 4u);
@@ -975,18 +1071,81 @@ __device__ __forceinline__ void run_down(const LayerArgs &a, Shared<NB> &sh, int
         }
         __builtin_amdgcn_s_sleep(2);
 #pragma unroll
-        for (int q = 0; q < kSlices; ++q)
-          if (q < a.n_slices && uint32_t(w[q] >> 32) != sh.ep)
-            w[q] = ld_dev(a.l.opart + (size_t(q) * kMaxNb + b) * H + r);
+        for (int t = 0; t < 4; ++t) ld_dev_u64x2(a.l.act, off + 16 * t, v[2 * t], v[2 * t + 1]);
       }
-      float v = 0.0f;
+      float f[8];
 #pragma unroll
-      for (int q = 0; q < kSlices; ++q)
-        if (q < a.n_slices) v += __uint_as_float(uint32_t(w[q]));
-      a.l.out[size_t(b) * H + r] = v;
+      for (int e = 0; e < 8; ++e) f[e] = i < n_items ? __uint_as_float(uint32_t(v[e])) : 0.0f;
+      half8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float fv = f[(e & 1) * 4 + (e >> 1)];   // element e holds column (0,4,1,5,2,6,3,7)[e]
+        hi[e] = _Float16(fv);
+        lo[e] = _Float16(fv - float(hi[e]));
+      }
+      if (i < n_items) {
+        const int fi = ((sl * 2 + (blk & 1)) * 4 + (blk >> 1)) * 8 + b;
+        frag[fi] = __builtin_bit_cast(uint4, hi);
+        frag[fi + 4] = __builtin_bit_cast(uint4, lo);
+      }
+      const float cs = group8_sum(((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7])));
+      if (i < n_items && blk == 0) gsum[sl * 4 + b] = cs;
+    }
+    __syncthreads();
+    // 4. the wave's slots
+#pragma unroll
+    for (int m = 0; m < kDownSlots; ++m) {
+      const int sl = par + 2 * m, slot = s0 + sl;
+      const int bt = slot < n_slots ? sh.dbits[slot] : 0;
+      if (bt == 0) continue;
+      half8 A0, A1;
+      if (bt == 4) {
+        A0 = word_to_a(cw[m].x);
+        A1 = word_to_a(cw[m].y);
+      } else {
+        // 3-bit: the high bits of the slot word's codes are nibble q % 2 of
+        // each byte of its chunk's high word
+        const uint32_t hb = bt == 3 ? (cw[m].y >> (4 * (q & 1))) & 0x0F0F0F0Fu : 0u;
+        if (bt == 3) lowbit_to_a<3>(cw[m].x, hb, A0, A1);
+        else lowbit_to_a<2>(cw[m].x, 0u, A0, A1);
+      }
+      const uint4 b0 = frag[((sl * 2 + 0) * 4 + q) * 8 + (j & 7)];
+      const uint4 b1 = frag[((sl * 2 + 1) * 4 + q) * 8 + (j & 7)];
+      // column j < 4: high half of row j (with the bias term); 4..7: low
+      // half; 8..15 and rows past NB (never staged): nothing
+      const bool live = j < 8 && (j & 3) < NB;
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, __builtin_bit_cast(half8, live ? b0 : z), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, __builtin_bit_cast(half8, live ? b1 : z), acc, 0, 0, 0);
+      const float wsl = live ? sh.wslot[(j & 3) < NB ? (j & 3) : 0][slot] : 0.0f;
+      const float gs = live && j < 4 ? gsum[sl * 4 + (j & 3)] : 0.0f;
+      const uint32_t s4[4] = {sbv[m].x, sbv[m].y, sbv[m].z, sbv[m].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tot[i] = fmaf(wsl, fmaf(sb_scale(s4[i]), acc[i], sb_bias(s4[i]) * gs), tot[i]);
     }
   }
+  // rows 4q + i, column j of the wave -> LDS; a row's value for row b of x
+  // is the sum over both parity waves of columns b and 4 + b
   __syncthreads();
+  if (j < 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(wave * 16 + 4 * q + i) * 8 + j] = tot[i];
+  }
+  __syncthreads();
+  if (threadIdx.x < kRowsPerTile * NB) {
+    const int rr = threadIdx.x % kRowsPerTile, b = threadIdx.x / kRowsPerTile;
+    const int rbk = rr / 16, r = rr % 16;
+    float v = 0.0f;
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      const int w = rbk + 2 * pr;
+      v += red[(w * 16 + r) * 8 + b] + red[(w * 16 + r) * 8 + 4 + b];
+    }
+    st_dev(a.l.opart + (size_t(x) * kMaxNb + b) * H + tile * kRowsPerTile + rr,
+           (uint64_t(sh.ep) << 32) | __float_as_uint(v));
+  }
+  combine_tile<NB>(a, sh, x, tile);
 }
 
 // ---------------------------------------------------------------- kernel
@@ -1125,7 +1284,11 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
       const int slot = i / a.ups;
       gate_up_item<NB, CPL, kM>(a, x, sh.desc[slot], slot, i - slot * a.ups, xs, xsum, xb, xg, red, sh.ep);
     }
-    for (; i < n_total; i += P) run_down<NB>(a, sh, x, i - n_gu, act_lds, asum_lds);
+    if constexpr (kM) {
+      for (; i < n_total; i += P) run_down_m<NB>(a, sh, x, i - n_gu, xb, xg, red);
+    } else {
+      for (; i < n_total; i += P) run_down<NB>(a, sh, x, i - n_gu, act_lds, asum_lds);
+    }
   }
 
   // two-level exit count; the last block out resets the counters
@@ -1197,7 +1360,9 @@ hipError_t launch_layer(const LayerLaunch &l, hipStream_t s) {
   a.tiles = l.hidden / kRowsPerTile;
   if (a.tiles > kMaxDownTiles || a.W / kChunk > 8 || a.W % kTileRowPairs) return hipErrorInvalidValue;
   const bool two = l.hidden > 64 * kChunk;
-  const bool mfma = l.hidden == kMfmaHidden;   // gate/up units on MFMA for two to four rows
+  // two to four rows at H = 2048 and 64 columns per slice: gate/up units and
+  // down tiles on MFMA
+  const bool mfma = l.hidden == kMfmaHidden && a.W == kGroup;
   switch (l.nb) {
     case 1: return two ? launch_nb<1, 2, false>(a, s) : launch_nb<1, 1, false>(a, s);
     case 2: return two ? launch_nb<2, 2, false>(a, s) : mfma ? launch_nb<2, 1, true>(a, s) : launch_nb<2, 1, false>(a, s);

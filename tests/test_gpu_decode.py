@@ -95,6 +95,53 @@ def test_full_shape_layers(moe, name, nb):
     assert moe.workspace_status(run.bufs.ws) == 0
 
 
+@pytest.mark.parametrize("name", ["verify_nb4", "lowbit_q3", "lowbit_q2", "mixed_q4q2"])
+@pytest.mark.parametrize("nb", [2, 3, 4])
+def test_full_shape_independent_rows(moe, name, nb):
+    """Full-shape layers (H 2048, I 512: the MFMA gate/up units and down
+    tiles) with 2..4 independent rows, so that at four rows the union passes
+    16 slots and the down tiles run more than one batch of slots."""
+    cfg = dataclasses.replace(syn.CONFIGS[name], x_mode="iid")
+    _say(f"[full-shape independent] {name} nb={nb}")
+    p = syn.make_problem(cfg, seed=5, device="cuda", n_layers=1)
+    run = DecodeRunner(moe, p)
+    x = _x(cfg, 21 + nb, nb, cfg.hidden, "cuda")
+    g = run.forward(x, 0)
+    r = oracle_layer(p, x.cpu().numpy(), 0)
+    st = compare_decode(g, r, cfg.top_k, f"{name} nb {nb}")
+    _say(f"   |U|={st['union']} rel err {st['rel']:.2e}")
+    if nb == 4:
+        assert st["union"] > 16
+    assert moe.workspace_status(run.bufs.ws) == 0
+
+
+def test_full_shape_bad_descriptor(moe):
+    """A routed descriptor past the pool in a full-shape four-row layer (MFMA
+    kernel): the record is skipped in every row that routed to it, the status
+    word is flagged, and the rest matches the oracle without it."""
+    cfg = dataclasses.replace(syn.CONFIGS["verify_nb4"], x_mode="iid")
+    p = syn.make_problem(cfg, seed=6, device="cuda", n_layers=1)
+    x = _x(cfg, 33, 4, cfg.hidden, "cuda")
+    r = oracle_layer(p, x.cpu().numpy(), 0)
+    bad_e = int(r["topk_idx"][1, 0])
+    rec = p.rec.clone()
+    rec[0, bad_e] = (p.pool.numel() + 4096) & ~0xFF
+    run = DecodeRunner(moe, dataclasses.replace(p, rec=rec))
+    g = run.forward(x, 0)
+    assert moe.workspace_status(run.bufs.ws) & 1
+    Wg, Wu, Wd = mo.read_expert(PoolView(p.pool), int(p.rec[0, bad_e]), cfg.hidden, cfg.inter)
+    expect = r["out_f64"].copy()
+    xn = x.cpu().numpy().astype(np.float64)
+    for b in range(4):
+        hit = np.nonzero(r["topk_idx"][b] == bad_e)[0]
+        if hit.size:
+            y, _ = mo.expert_mlp(Wg, Wu, Wd, xn[b])
+            expect[b] -= r["topk_w"][b, hit[0]] * y
+    err = np.abs(g["out"] - expect).max()
+    assert err <= 1e-3 * np.abs(expect).max()
+    assert moe.workspace_status(run.bufs.ws) == 0     # read-and-clear
+
+
 def test_route_only_matches_forward(moe):
     cfg = syn.CONFIGS["verify_nb4"]
     p = syn.make_problem(cfg, seed=2, device="cuda", n_layers=1)
