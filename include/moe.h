@@ -99,7 +99,8 @@ typedef struct moe_pool {
 } moe_pool;
 
 /* The shared expert (load.rs Moe: shared_expert_gate.weight and the shared
- * gate/up/down projections); always 4-bit ("dense projections stay Q4"). */
+ * gate/up/down projections); always 4-bit (the pages keep every dense
+ * projection at 4 bits when routed experts go to 3 or 2). */
 typedef struct moe_shared {
     const uint16_t *gate;     /* device, bf16 [H] sigmoid gate vector, 16-byte aligned */
     uint64_t rec;             /* descriptor of its 4-bit record, tag 0 */

@@ -8,11 +8,11 @@ float64, written as the plain definition of what the layer computes.
 What is computed (sources are the three pages on the qwen4_exp GPU engine:
 the rustdoc page "Struct Gpu", and the source pages gpu.rs and gpu/load.rs):
 
-* Dequantisation (gpu.rs, struct ``Q`` "Affine-Q4 projection"; load.rs, the
+* Dequantisation (gpu.rs, struct ``Q``, the affine 4-bit projection; load.rs, the
   ``q`` closure that reads ``.weight``/``.scales``/``.biases``; the
   expert-width check naming the 64-code quantisation group):
   W[o][i] = q[o][i] * s[o][i // 64] + b[o][i // 64].
-* Router (Struct Gpu, ``router_b``: "softmax over experts, top-k"; the router
+* Router (Struct Gpu, ``router_b``: softmax over the router logits, then top-k; the router
   weight is the bf16 tensor ``mlp.gate.weight`` of load.rs):
   logits[b][e] = sum_i R[e][i] * x[b][i].
 * Top-k: the k largest logits, ties to the lower expert id, ordered by

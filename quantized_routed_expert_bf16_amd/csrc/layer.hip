@@ -1,11 +1,12 @@
 // The whole decode MoE layer in one persistent launch (gfx950).
 //
-// What it computes is Struct Gpu router_b ("softmax over experts, top-k" over
-// nb rows) followed by experts_b (the routed experts of the union published
-// in the slot table, plus the shared expert, summed per row), with the union
-// and slot table of gpu.rs (union_of: first-seen order; slot_tab entry 62 =
-// resident count, 63 = union size; wmap = per-row weight per slot) built on
-// the device instead of by a host round trip.
+// What it computes is Struct Gpu router_b (a softmax over the router logits
+// and a top-k selection, for nb rows) followed by experts_b (the routed
+// experts of the union published in the slot table, plus the shared expert,
+// summed per row), with the union and slot table of gpu.rs (union_of:
+// first-seen order; slot_tab entry 62 = resident count, 63 = union size;
+// wmap = per-row weight per slot) built on the device instead of by a host
+// round trip.
 //
 // XCD-aware split.  The grid is 8 slices of blocks (block b belongs to slice
 // b % 8, which the round-robin dispatcher places on XCD b % 8).  Slice x owns
@@ -14,21 +15,25 @@
 // for every slot of the union.  A slice therefore needs nothing from other
 // slices until the very end:
 //   1. every block stages the nb rows of x in LDS (plus per-32 sums of x);
-//   2. each slice computes the whole router itself (E expert rows + the
-//      shared gate vector as row E, float64 accumulation) -- 512 KB read per
-//      slice, mostly served by the memory-side cache -- and publishes the
-//      logits in its own buffer; meanwhile other blocks of the slice run the
-//      shared expert's gate/up rows, which need no routing;
-//   3. every block of the slice waits for the slice's router blocks, then
-//      ranks the logits and builds the union itself (wave-parallel);
-//   4. gate/up units (slot, 8 row pairs of the slice) write silu(g)*u;
-//      down units (tile of 32 output rows) first load their weights for all
-//      slots, then wait for the slice's gate/up units, and write the slice's
-//      routing-weighted partial rows (sum over slots in slot order, shared
-//      expert last);
-//   5. the slice that completes a row tile last sums the slices' partials in
-//      slice order into `out`;
-//   6. the last block out resets the counters for the next launch.
+//   2. router blocks, numbered across the slices, compute the E expert rows
+//      and the shared gate vector (row E) with float64 accumulation, publish
+//      the logits and bump a counter in every slice; meanwhile the other
+//      blocks run the shared expert's gate/up units, which need no routing;
+//   3. every block waits for its slice's router count, then selects each
+//      row's top-k and builds the union itself (wave-parallel);
+//   4. gate/up units (slot, 8 row pairs of the slice) write silu(g)*u tagged
+//      with the call's epoch and bump the slice's gate/up counter; down
+//      tiles (32 output rows) load their weights for all slots, wait for the
+//      slice's gate/up count, and publish the slice's routing-weighted
+//      partial rows (sum over slots in slot order, shared expert last);
+//   5. the block of slice (tile mod slices) sums every slice's partial of a
+//      tile in slice order into `out`, re-reading partials whose epoch tag
+//      is not yet this call's;
+//   6. the last block out publishes the epoch and resets the counters.
+// Two to four rows at H = 2048 with 64 columns per slice run a second
+// instantiation (kM) whose gate/up units and down tiles are MFMA
+// contractions on exact f16 codes and f16 high/low halves of x and act; the
+// others run the same steps on the VALU with in-register dequantisation.
 // Cross-block data moves through device-coherent loads/stores (see
 // device_common.h), so results do not depend on where blocks actually run;
 // the slice-to-XCD placement only keeps the polling local.  Every wait is

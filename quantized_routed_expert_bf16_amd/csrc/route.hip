@@ -1,8 +1,9 @@
 // Router matvec, top-k softmax, union and slot table of one decode step
 // (moe_route without the experts), for gfx950.
 //
-// Struct Gpu router_b: "softmax over experts, top-k" for nb rows; gpu.rs
-// union_of: "unique entries in first-seen order"; gpu.rs slot_tab / wmap field
+// Struct Gpu router_b: softmax over the router logits and top-k selection
+// for nb rows; gpu.rs union_of: the distinct experts in the order they are
+// first met; gpu.rs slot_tab / wmap field
 // docs: 64 descriptors per layer, entry 62 = resident count, 63 = union size,
 // per-row routing weight per slot.
 //
