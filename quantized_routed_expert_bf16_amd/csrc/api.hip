@@ -149,24 +149,42 @@ static int check_slots(const moe_slots *s, const moe_dims &d, int nb) {
   return check_ws(s->ws, s->ws_bytes, d, nb);
 }
 
-static RouteArgs route_args(const float *x, int rows, const moe_router *r, const moe_shared *sh,
-                            double *logits, float *gamma, uint32_t *topk_idx, float *topk_w,
-                            void *ws) {
-  RouteArgs a{};
-  a.x = x;
-  a.router = r->weight;
-  a.gvec = sh->gate;
-  a.rec = r->rec;
-  a.hidden = r->dims.hidden;
-  a.n_experts = r->dims.n_experts;
-  a.top_k = r->dims.top_k;
-  a.rows = rows;
-  a.logits = logits;
-  a.gamma = gamma;
-  a.topk_idx = topk_idx;
-  a.topk_w = topk_w;
-  a.counter = static_cast<uint32_t *>(ws) + kSyncRoute;
-  return a;
+
+// The decode launch description shared by moe_route (no pool, no output)
+// and moe_layer_forward; arguments were validated by the caller.
+static LayerLaunch layer_launch(const float *x, int nb, const moe_router *router, const moe_slots *slots,
+                                const moe_pool *pool, const moe_shared *shared, float *out) {
+  const moe_dims &d = router->dims;
+  const WorkspaceLayout L = workspace_layout(d.hidden, d.inter, d.n_experts, d.top_k, nb);
+  uint8_t *ws = static_cast<uint8_t *>(slots->ws);
+  LayerLaunch l{};
+  l.x = x;
+  l.nb = nb;
+  l.router = router->weight;
+  l.gvec = shared->gate;
+  l.rec = router->rec;
+  l.pool = pool ? pool->base : nullptr;
+  l.pool_bytes = pool ? pool->bytes : 0;
+  l.shared_rec = shared->rec;
+  l.hidden = d.hidden;
+  l.inter = d.inter;
+  l.n_experts = d.n_experts;
+  l.top_k = d.top_k;
+  l.logits = slots->logits;
+  l.gamma = slots->gamma;
+  l.topk_idx = slots->topk_idx;
+  l.topk_w = slots->topk_w;
+  l.tab = slots->tab;
+  l.wmap = slots->wmap;
+  l.ids = slots->ids;
+  l.out = out;
+  l.sync = reinterpret_cast<uint32_t *>(ws + L.counters);
+  l.act = reinterpret_cast<uint64_t *>(ws + L.act);
+  l.opart = reinterpret_cast<uint64_t *>(ws + L.opart);
+  l.slice_logits = reinterpret_cast<double *>(ws + L.slice_logits);
+  l.slice_gamma = reinterpret_cast<float *>(ws + L.slice_logits +
+                                            size_t(kSlices) * kMaxNb * kMaxExperts * sizeof(double));
+  return l;
 }
 
 }  // namespace moe
@@ -205,12 +223,8 @@ int moe_route(const float *x, int32_t nb, const moe_router *router, const moe_sh
   REQ(x, 16, "x");
   if ((rc = check_shared(shared, d, nullptr))) return rc;
   if ((rc = check_slots(slots, d, nb))) return rc;
-  RouteArgs a = route_args(x, nb, router, shared, slots->logits, slots->gamma, slots->topk_idx,
-                           slots->topk_w, slots->ws);
-  a.tab = slots->tab;
-  a.wmap = slots->wmap;
-  a.ids = slots->ids;
-  rc = launched(launch_route(a, static_cast<hipStream_t>(stream)), "route");
+  const LayerLaunch l = layer_launch(x, nb, router, slots, nullptr, shared, nullptr);
+  rc = launched(launch_route_only(l, static_cast<hipStream_t>(stream)), "route");
   return rc ? rc : ok();
 }
 
@@ -227,35 +241,7 @@ int moe_layer_forward(const float *x, int32_t nb, const moe_router *router, moe_
   if ((rc = check_slots(slots, d, nb))) return rc;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const WorkspaceLayout L = workspace_layout(d.hidden, d.inter, d.n_experts, d.top_k, nb);
-  uint8_t *ws = static_cast<uint8_t *>(slots->ws);
-  LayerLaunch l{};
-  l.x = x;
-  l.nb = nb;
-  l.router = router->weight;
-  l.gvec = shared->gate;
-  l.rec = router->rec;
-  l.pool = pool->base;
-  l.pool_bytes = pool->bytes;
-  l.shared_rec = shared->rec;
-  l.hidden = d.hidden;
-  l.inter = d.inter;
-  l.n_experts = d.n_experts;
-  l.top_k = d.top_k;
-  l.logits = slots->logits;
-  l.gamma = slots->gamma;
-  l.topk_idx = slots->topk_idx;
-  l.topk_w = slots->topk_w;
-  l.tab = slots->tab;
-  l.wmap = slots->wmap;
-  l.ids = slots->ids;
-  l.out = out;
-  l.sync = reinterpret_cast<uint32_t *>(ws + L.counters);
-  l.act = reinterpret_cast<uint64_t *>(ws + L.act);
-  l.opart = reinterpret_cast<uint64_t *>(ws + L.opart);
-  l.slice_logits = reinterpret_cast<double *>(ws + L.slice_logits);
-  l.slice_gamma = reinterpret_cast<float *>(ws + L.slice_logits +
-                                            size_t(kSlices) * kMaxNb * kMaxExperts * sizeof(double));
+  const LayerLaunch l = layer_launch(x, nb, router, slots, pool, shared, out);
   if ((rc = launched(launch_layer(l, s), "layer"))) return rc;
   if ((rc = stage_done(0, s))) return rc;
   return ok();

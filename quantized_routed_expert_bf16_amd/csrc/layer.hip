@@ -1153,6 +1153,44 @@ __device__ __forceinline__ void run_down_m(const LayerArgs &a, Shared<NB> &sh, i
   combine_tile<NB>(a, sh, x, tile);
 }
 
+// The nb rows of x into LDS, chunk-major (ChunkX), and their per-32 sums.
+// All of a thread's loads are in flight at once.
+template <int NB, int CPL>
+__device__ __forceinline__ void stage_x(const LayerArgs &a, float *xs, float *xsum) {
+  const int H = a.l.hidden;
+  {   // all of the thread's x loads in flight at once (H <= 2048 CPL)
+    constexpr int kXIt = 2 * NB * CPL;
+    float4 xv[kXIt];
+#pragma unroll
+    for (int t = 0; t < kXIt; ++t) {   // unconditional loads keep xv in registers
+      const int i = min((threadIdx.x + t * kThreads) * 4, NB * H - 4);
+      xv[t] = *reinterpret_cast<const float4 *>(a.l.x + i);
+    }
+    const int nch = H / kChunk;
+#pragma unroll
+    for (int t = 0; t < kXIt; ++t) {   // float4 f of row b -> group f % 8 of chunk f / 8
+      const int i = threadIdx.x + t * kThreads;
+      if (i * 4 < NB * H) {
+        const int b = i / (H / 4), f = i - b * (H / 4);
+        reinterpret_cast<float4 *>(xs)[(b * 8 + f % 8) * nch + f / 8] = xv[t];
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < NB * (H / kChunk); i += kThreads) {   // per-32 sums
+    const int b = i / (H / kChunk), c = i - b * (H / kChunk);
+    const ChunkX X{reinterpret_cast<const float4 *>(xs), H / kChunk, c};
+    float sm = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kChunk / 4; ++q) {
+      const float4 f = X(b, q);
+      sm += (f.x + f.y) + (f.z + f.w);
+    }
+    xsum[i] = sm;
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------- kernel
 template <int NB, int CPL, bool kM>
 __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
@@ -1192,37 +1230,7 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
     RouterRow<CPL> rrow;
     if (route) router_prefetch<CPL>(a, g, rrow);
     for (int e = threadIdx.x; e < a.l.n_experts; e += kThreads) rec_lds[e] = a.l.rec[e];
-    {   // all of the thread's x loads in flight at once (H <= 2048 CPL)
-      constexpr int kXIt = 2 * NB * CPL;
-      float4 xv[kXIt];
-#pragma unroll
-      for (int t = 0; t < kXIt; ++t) {   // unconditional loads keep xv in registers
-        const int i = min((threadIdx.x + t * kThreads) * 4, NB * H - 4);
-        xv[t] = *reinterpret_cast<const float4 *>(a.l.x + i);
-      }
-      const int nch = H / kChunk;
-#pragma unroll
-      for (int t = 0; t < kXIt; ++t) {   // float4 f of row b -> group f % 8 of chunk f / 8
-        const int i = threadIdx.x + t * kThreads;
-        if (i * 4 < NB * H) {
-          const int b = i / (H / 4), f = i - b * (H / 4);
-          reinterpret_cast<float4 *>(xs)[(b * 8 + f % 8) * nch + f / 8] = xv[t];
-        }
-      }
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < NB * (H / kChunk); i += kThreads) {   // per-32 sums
-      const int b = i / (H / kChunk), c = i - b * (H / kChunk);
-      const ChunkX X{reinterpret_cast<const float4 *>(xs), H / kChunk, c};
-      float sm = 0.0f;
-#pragma unroll
-      for (int q = 0; q < kChunk / 4; ++q) {
-        const float4 f = X(b, q);
-        sm += (f.x + f.y) + (f.z + f.w);
-      }
-      xsum[i] = sm;
-    }
-    __syncthreads();
+    stage_x<NB, CPL>(a, xs, xsum);
 
     double *lg = a.l.slice_logits;
     float *gm = a.l.slice_gamma;
@@ -1309,6 +1317,47 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
   }
 }
 
+// moe_route: the routing steps of the layer kernel alone.  Every block is a
+// router block (rows 4 g .. of router block g); block 0 then selects each
+// row's top-k, builds the union and writes the caller's tables, exactly as
+// block 0 of the layer kernel does.
+template <int NB, int CPL>
+__global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
+  extern __shared__ float4 dyn[];
+  __shared__ Shared<NB> sh;
+  __shared__ uint64_t rec_lds[kMaxExperts];
+  const int H = a.l.hidden;
+  float *xs = reinterpret_cast<float *>(dyn);           // [NB][H]
+  float *xsum = xs + NB * H;                            // [NB][H/32]
+  float *keys = xsum + NB * (H / kChunk);               // routing build scratch
+  if (threadIdx.x == 0) {
+    const uint32_t e = ld_dev(a.l.sync + kSyncEpoch) + 1u;
+    sh.ep = e ? e : 1u;
+  }
+  const int g = blockIdx.x;
+  RouterRow<CPL> rrow;
+  router_prefetch<CPL>(a, g, rrow);
+  if (g == 0)
+    for (int e = threadIdx.x; e < a.l.n_experts; e += kThreads) rec_lds[e] = a.l.rec[e];
+  stage_x<NB, CPL>(a, xs, xsum);
+  router_rows<NB, CPL>(a, xs, g, rrow, a.l.slice_logits, a.l.slice_gamma);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(sw(a, 0, kSliceRoute), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (g == 0) {
+    wait_geq(a, sw(a, 0, kSliceRoute), uint32_t(gridDim.x));
+    route_select<NB>(a, sh, a.l.slice_logits, a.l.slice_gamma, reinterpret_cast<uint8_t *>(keys));
+    route_union<NB>(a, sh, rec_lds);
+  }
+  // the last block out publishes the epoch and resets the counters
+  block_signal(a.l.sync + kSyncExit, 1u, &sh.prev);
+  __syncthreads();
+  if (sh.prev == gridDim.x - 1)
+    for (int i = threadIdx.x; i < kSyncWords; i += kThreads)
+      if (i != kSyncStatus) st_dev(a.l.sync + i, i == kSyncEpoch ? sh.ep : 0u);
+}
+
 size_t dyn_lds_bytes(int nb, int hidden, bool mfma) {
   // x, its per-32 sums and the logit keys (and with MFMA gate/up units the B
   // fragments, group sums and partial rows); or one batch of staged act
@@ -1354,7 +1403,30 @@ hipError_t launch_nb(LayerArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int NB, int CPL>
+hipError_t launch_route_nb(LayerArgs &a, hipStream_t s) {
+  const int H = a.l.hidden;
+  const size_t lds = sizeof(float) * (size_t(NB) * H + size_t(NB) * (H / kChunk) + size_t(kKeyFloats) * NB);
+  hipLaunchKernelGGL((route_kernel<NB, CPL>), dim3(a.route_blocks), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_route_only(const LayerLaunch &l, hipStream_t s) {
+  LayerArgs a{};
+  a.l = l;
+  a.n_slices = 1;
+  a.route_blocks = (l.n_experts + 1 + kWaves - 1) / kWaves;
+  a.per_slice = a.route_blocks;
+  const bool two = l.hidden > 64 * kChunk;
+  switch (l.nb) {
+    case 1: return two ? launch_route_nb<1, 2>(a, s) : launch_route_nb<1, 1>(a, s);
+    case 2: return two ? launch_route_nb<2, 2>(a, s) : launch_route_nb<2, 1>(a, s);
+    case 3: return two ? launch_route_nb<3, 2>(a, s) : launch_route_nb<3, 1>(a, s);
+    default: return two ? launch_route_nb<4, 2>(a, s) : launch_route_nb<4, 1>(a, s);
+  }
+}
 
 hipError_t launch_layer(const LayerLaunch &l, hipStream_t s) {
   LayerArgs a{};

@@ -45,27 +45,6 @@ __host__ __device__ inline int bits_of_tag(uint64_t desc) {
 }
 
 // ------------------------------------------------------------ arguments
-struct RouteArgs {
-  const float *x;          // [rows][H]
-  const uint16_t *router;  // [E][H] bf16
-  const uint16_t *gvec;    // [H] bf16
-  const uint64_t *rec;     // [E]
-  int hidden, n_experts, top_k, rows;
-  double *logits;          // [rows][E]
-  float *gamma;            // [rows]
-  uint32_t *topk_idx;      // [rows][k]
-  float *topk_w;           // [rows][k]
-  // decode outputs (may be null for prefill)
-  uint64_t *tab;           // [64]
-  float *wmap;             // [4][64]
-  uint32_t *ids;           // [64]
-  // prefill outputs (may be null for decode)
-  int32_t *expert_ptr;     // [E+1]
-  int32_t *entry_row;      // [t*k]
-  int32_t *entry_rank;     // [t*k]
-  uint32_t *counter;       // one zero-initialised word, reset by the last block
-};
-
 // One decode layer launch (the fused persistent kernel of layer.hip).
 struct LayerLaunch {
   const float *x;            // [nb][H]
@@ -118,7 +97,7 @@ constexpr int kSyncSliceStride = 64;        // slice x owns words [64x, 64x + 64
 constexpr int kSliceRoute = 0;              //   router blocks of the slice arrived
 constexpr int kSliceGu = 32;                //   gate/up units of the slice done
 constexpr int kSliceExit = 48;              //   blocks of the slice that left
-constexpr int kSyncRoute = 512;             // standalone route kernel: blocks arrived
+constexpr int kSyncRoute = 512;             // prefill top-k kernel: blocks arrived
 constexpr int kSyncStatus = 520;            // bit 0: bad descriptor skipped; bit 2: a wait ran out
 constexpr int kSyncExit = 528;              // slices whose blocks all left
 constexpr int kSyncAbort = 576;             // set when a wait ran out: all waits fall through
@@ -127,9 +106,8 @@ constexpr int kSyncTile = 640;              // 256 words: slices done per down r
 constexpr int kMaxDownTiles = 256;
 
 // ------------------------------------------------------------- launchers
-hipError_t launch_route(const RouteArgs &a, hipStream_t s);
+hipError_t launch_route_only(const LayerLaunch &l, hipStream_t s);   // moe_route
 hipError_t launch_layer(const LayerLaunch &l, hipStream_t s);
-int decode_rows_per_tile(int inter);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 
 struct PrefillArgs {
