@@ -1266,18 +1266,42 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     if (early) d0 = rec_lds[sh.sel[0][slot0]];
     if constexpr (kM) {
-      GuRegsM pre;
-      // (4-bit records only: the early loads stay out of the other widths'
-      // register budget)
+      // the block's units i, i + P, ... < n_gu run as a pipeline: the next
+      // unit's weights are in flight while the current one computes.  When
+      // the first unit's slot is one of row 0's ranks (a 4-bit record: the
+      // early loads stay out of the other widths' register budget) its
+      // weights load while the union is built.
+      GuRegsM cur, nxt;
       const bool em = early && bits_of_tag(d0) == 4 && record_ok(d0, a.l.pool_bytes, a.l.hidden, a.l.inter);
-      if (em) gate_up_load_m<4>(a, d0, x, i - slot0 * a.ups, pre);
+      if (em) gate_up_load_m<4>(a, d0, x, i - slot0 * a.ups, cur);
       asm volatile("" ::: "memory");   // the loads are issued here, not sunk to their use
       route_union<NB>(a, sh, rec_lds);
-      if (em) {   // slot0 < k <= u: a gate/up unit
-        gate_up_unit_m<NB, 4>(a, pre, x, i - slot0 * a.ups, slot0, xb, xg, red, reinterpret_cast<uint32_t *>(xs),
-                              sh.ep);
-        gate_up_signal(a, x);
-        i += P;
+      const int n_gu0 = sh.u * a.ups;
+      auto load_unit = [&](int it, GuRegsM &r) {
+        const int slot = it / a.ups;
+        const uint64_t d = sh.desc[slot];
+        if (record_ok(d, a.l.pool_bytes, a.l.hidden, a.l.inter)) gate_up_load_m_any(a, d, x, it - slot * a.ups, r);
+      };
+      if (!em && i < n_gu0) load_unit(i, cur);
+      while (i < n_gu0) {
+        const int nx = i + P;
+        if (nx < n_gu0) load_unit(nx, nxt);
+        asm volatile("" ::: "memory");
+        const int slot = i / a.ups, unit = i - slot * a.ups;
+        const uint64_t d = sh.desc[slot];
+        uint32_t *stg = reinterpret_cast<uint32_t *>(xs);
+        if (record_ok(d, a.l.pool_bytes, a.l.hidden, a.l.inter)) {
+          switch (bits_of_tag(d)) {
+            case 4: gate_up_unit_m<NB, 4>(a, cur, x, unit, slot, xb, xg, red, stg, sh.ep); break;
+            case 3: gate_up_unit_m<NB, 3>(a, cur, x, unit, slot, xb, xg, red, stg, sh.ep); break;
+            default: gate_up_unit_m<NB, 2>(a, cur, x, unit, slot, xb, xg, red, stg, sh.ep); break;
+          }
+          gate_up_signal(a, x);
+        } else {
+          gate_up_bad<NB>(a, x, slot, unit, sh.ep);
+        }
+        cur = nxt;
+        i = nx;
       }
     } else {
       GuRegs<CPL> pre;
@@ -1293,9 +1317,11 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
     const int u = sh.u;
     const int n_gu = u * a.ups;
     const int n_total = n_gu + a.tiles;
-    for (; i < n_gu; i += P) {
-      const int slot = i / a.ups;
-      gate_up_item<NB, CPL, kM>(a, x, sh.desc[slot], slot, i - slot * a.ups, xs, xsum, xb, xg, red, sh.ep);
+    if constexpr (!kM) {
+      for (; i < n_gu; i += P) {
+        const int slot = i / a.ups;
+        gate_up_item<NB, CPL, kM>(a, x, sh.desc[slot], slot, i - slot * a.ups, xs, xsum, xb, xg, red, sh.ep);
+      }
     }
     if constexpr (kM) {
       for (; i < n_total; i += P) run_down_m<NB>(a, sh, x, i - n_gu, xb, xg, red);
