@@ -57,7 +57,6 @@ constexpr int kStagePad = 4;                          // floats after each stage
 // staged act floats per row of x: (slot groups x kSlotBatch) runs of W + pad, W >= 32
 constexpr int kStageFloats = kStageCols * kSlotBatch + (kStageCols / kChunk) * kSlotBatch * kStagePad;
 constexpr uint32_t kSpinLimit = 1u << 22;
-constexpr int kKeyFloats = 16 * (8 + 8 + 4) / 4;       // routing select scratch per row: keys, values, ids
 
 struct LayerArgs {
   LayerLaunch l;
@@ -98,7 +97,7 @@ __device__ inline void wait_geq(const LayerArgs &a, const uint32_t *p, uint32_t 
 
 template <int NB>
 struct Shared {
-  double exq[64];
+  float exq[64];
   int sel[NB][kMaxTopK];
   double selv[NB][kMaxTopK];
   float wsel[NB][kMaxTopK];
@@ -195,17 +194,15 @@ __device__ __forceinline__ void router_rows(const LayerArgs &a, const float *xs,
 // k keys reach; it stops early once exactly k do.  Keys above T are selected
 // and, of the keys equal to T (equal logits), the lowest ids fill the
 // remaining places, which is the order (logit descending, id ascending).
-// The k entries are packed into LDS in id order and ranked against each
-// other: s.sel[b][rank] and s.selv[b][rank] on return, for every wave.
+// The k selected entries are ranked against each other in registers (the
+// wave walks the selected lanes with readlane): s.sel[b][rank] and
+// s.selv[b][rank] on return.
 // kJ = 2 serves up to 128 experts, 4 up to 256.
 template <int NB, int kJ>
 __device__ __forceinline__ void select_row(const LayerArgs &a, Shared<NB> &s, const double *lg, const float *gm,
-                           uint8_t *kbuf, int b) {
+                           int b) {
   const int lane = threadIdx.x & 63;
   const int E = a.l.n_experts, k = a.l.top_k;
-  uint64_t *ck = reinterpret_cast<uint64_t *>(kbuf) + b * 16;                 // [NB][16] keys
-  double *cv = reinterpret_cast<double *>(kbuf) + NB * 16 + b * 16;           // values
-  int *cid = reinterpret_cast<int *>(reinterpret_cast<double *>(kbuf) + 2 * NB * 16) + b * 16;   // ids
   double v[kJ];
 #pragma unroll
   for (int j = 0; j < kJ; ++j)   // clamped and unconditional: all loads in flight at once
@@ -236,40 +233,39 @@ __device__ __forceinline__ void select_row(const LayerArgs &a, Shared<NB> &s, co
 #pragma unroll
   for (int j = 0; j < kJ; ++j) need -= __popcll(__ballot(kk[j] > T));
   const uint64_t below = (uint64_t(1) << lane) - 1;
-  int eq_before = 0, packed = 0;
+  int eq_before = 0;
+  bool take[kJ];
+  uint64_t tm[kJ];
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
     const bool eq = kk[j] == T;
     const uint64_t eqm = __ballot(eq);
-    const bool take = kk[j] > T || (eq && eq_before + __popcll(eqm & below) < need);
-    const uint64_t tm = __ballot(take);
-    if (take) {
-      const int ci = packed + __popcll(tm & below);
-      ck[ci] = kk[j];
-      cv[ci] = v[j] + 0.0;
-      cid[ci] = lane + 64 * j;
-    }
+    take[j] = kk[j] > T || (eq && eq_before + __popcll(eqm & below) < need);
+    tm[j] = __ballot(take[j]);
     eq_before += __popcll(eqm);
-    packed += __popcll(tm);
   }
-  __builtin_amdgcn_wave_barrier();
-  // rank of packed entry `lane` (LDS accesses of one wave complete in
-  // order, so the wave reads back what its lanes wrote)
-  const bool me = lane < k;
-  const uint64_t mk = ck[me ? lane : 0];
-  const int mid = cid[me ? lane : 0];
-  const double mv = cv[me ? lane : 0];
-  int rank = 0;
+  // rank the k selected entries against each other in registers: the
+  // wave walks the selected lanes (uniform masks) and reads each entry's
+  // key with readlane
+  int rank[kJ];
 #pragma unroll
-  for (int q = 0; q < kMaxTopK; ++q) {   // every read issued at once; q >= k masked
-    const uint64_t qk = ck[q];
-    const int qi = cid[q];
-    rank += int(q < k && pair_before(qk, qi, mk, mid));
+  for (int j = 0; j < kJ; ++j) rank[j] = 0;
+#pragma unroll
+  for (int jq = 0; jq < kJ; ++jq) {
+    for (uint64_t m = tm[jq]; m; m &= m - 1) {
+      const int L = __builtin_ctzll(m);
+      const uint64_t qk = readlane_u64(kk[jq], L);
+      const int qi = L + 64 * jq;
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) rank[j] += int(pair_before(qk, qi, kk[j], lane + 64 * j));
+    }
   }
-  if (me) {
-    s.sel[b][rank] = mid;
-    s.selv[b][rank] = mv;
-  }
+#pragma unroll
+  for (int j = 0; j < kJ; ++j)
+    if (take[j]) {
+      s.sel[b][rank[j]] = lane + 64 * j;
+      s.selv[b][rank[j]] = v[j] + 0.0;
+    }
   if (lane == 0) s.gam[b] = gam;
   if (blockIdx.x == 0) {   // caller-visible logits (as published)
 #pragma unroll
@@ -279,12 +275,11 @@ __device__ __forceinline__ void select_row(const LayerArgs &a, Shared<NB> &s, co
 }
 
 template <int NB>
-__device__ __forceinline__ void route_select(const LayerArgs &a, Shared<NB> &s, const double *lg, const float *gm,
-                             uint8_t *kbuf) {
+__device__ __forceinline__ void route_select(const LayerArgs &a, Shared<NB> &s, const double *lg, const float *gm) {
   const int wave = threadIdx.x >> 6;
   if (wave < NB) {
-    if (a.l.n_experts <= 128) select_row<NB, 2>(a, s, lg, gm, kbuf, wave);
-    else select_row<NB, kMaxExperts / 64>(a, s, lg, gm, kbuf, wave);
+    if (a.l.n_experts <= 128) select_row<NB, 2>(a, s, lg, gm, wave);
+    else select_row<NB, kMaxExperts / 64>(a, s, lg, gm, wave);
   }
   __syncthreads();
 }
@@ -304,7 +299,9 @@ __device__ __forceinline__ void route_union(const LayerArgs &a, Shared<NB> &s, c
     const int lb = ent ? lane / k : 0, lr = lane - lb * k;
     const int e_l = ent ? s.sel[lb][lr] : 0;
     const uint64_t d_l = ent ? rec_lds[e_l] : a.l.shared_rec;
-    const double ex = ent ? exp(s.selv[lb][lr] - s.selv[lb][0]) : 0.0;
+    // (float32: the weights are float32 results, within a few ulp of the
+    // float64 softmax)
+    const float ex = ent ? expf(float(s.selv[lb][lr] - s.selv[lb][0])) : 0.0f;
     s.exq[lane] = ex;
     // first-seen union: fq = lowest entry with this lane's expert
     int fq = lane;
@@ -319,14 +316,19 @@ __device__ __forceinline__ void route_union(const LayerArgs &a, Shared<NB> &s, c
     const int slot = __popcll(mask & ((uint64_t(1) << fq) - 1));
     const int u = __popcll(mask);
     __builtin_amdgcn_wave_barrier();
-    // softmax of each row's k selected logits, summed in rank order
-    double sum = 0.0;
+    // softmax of each row's k selected logits: with k = 8 a row's entries
+    // are one group of 8 lanes (DPP sum), else summed in rank order
+    float sum = 0.0f;
+    if (k == 8) {
+      sum = group8_sum(ex);
+    } else {
 #pragma unroll
-    for (int r = 0; r < kMaxTopK; ++r) {   // every read issued at once; adding 0 past k
-      const double e = s.exq[min(lb * k + r, 63)];
-      sum += r < k ? e : 0.0;
+      for (int r = 0; r < kMaxTopK; ++r) {   // every read issued at once; adding 0 past k
+        const float e = s.exq[min(lb * k + r, 63)];
+        sum += r < k ? e : 0.0f;
+      }
     }
-    const float w_l = ent ? float(ex / sum) : 0.0f;
+    const float w_l = ent ? ex / sum : 0.0f;
     if (ent) s.wsel[lb][lr] = w_l;
     if (lane == 0) s.u = u;
 #pragma unroll
@@ -1200,14 +1202,12 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
   const int H = a.l.hidden;
   // x and its sums live until the block's last gate/up unit; a block takes
   // its down tiles after all of its gate/up units, so the act staging of the
-  // down tiles reuses that space.  The logit keys sit past x: the routing
-  // build runs between the shared and the routed gate/up units.
+  // down tiles reuses that space.
   float *xs = reinterpret_cast<float *>(dyn);           // [NB][H]
   float *xsum = xs + NB * H;                            // [NB][H/32]
-  float *keys = xsum + NB * (H / kChunk);               // routing build scratch
-  // MFMA gate/up operands after the keys: B fragments, group sums, the
+  // MFMA gate/up operands after the sums: B fragments, group sums, the
   // waves' partial rows
-  uint4 *xb = reinterpret_cast<uint4 *>(keys + kKeyFloats * NB);
+  uint4 *xb = reinterpret_cast<uint4 *>(xsum + NB * (H / kChunk));
   float *xg = reinterpret_cast<float *>(xb) + (kM ? kMG * 256 : 0);
   float *red = xg + kMG * 8;
   float *act_lds = xs;                                  // [batch slots][NB][W + pad]
@@ -1252,7 +1252,7 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
       gate_up_item<NB, CPL, kM>(a, x, a.l.shared_rec, kSharedSlot, i, xs, xsum, xb, xg, red, sh.ep);
 
     wait_geq(a, sw(a, x, kSliceRoute), uint32_t(a.route_blocks));
-    route_select<NB>(a, sh, lg, gm, reinterpret_cast<uint8_t *>(keys));
+    route_select<NB>(a, sh, lg, gm);
     // the block's work items i0, i0 + P, ...: gate/up units first, then down
     // tiles (two loops, so neither carries the other's live values).  When
     // the first unit's slot is one of row 0's ranks its expert is known
@@ -1355,7 +1355,6 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
   const int H = a.l.hidden;
   float *xs = reinterpret_cast<float *>(dyn);           // [NB][H]
   float *xsum = xs + NB * H;                            // [NB][H/32]
-  float *keys = xsum + NB * (H / kChunk);               // routing build scratch
   if (threadIdx.x == 0) {
     const uint32_t e = ld_dev(a.l.sync + kSyncEpoch) + 1u;
     sh.ep = e ? e : 1u;
@@ -1373,7 +1372,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
     __hip_atomic_fetch_add(sw(a, 0, kSliceRoute), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (g == 0) {
     wait_geq(a, sw(a, 0, kSliceRoute), uint32_t(gridDim.x));
-    route_select<NB>(a, sh, a.l.slice_logits, a.l.slice_gamma, reinterpret_cast<uint8_t *>(keys));
+    route_select<NB>(a, sh, a.l.slice_logits, a.l.slice_gamma);
     route_union<NB>(a, sh, rec_lds);
   }
   // the last block out publishes the epoch and resets the counters
@@ -1385,11 +1384,10 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
 }
 
 size_t dyn_lds_bytes(int nb, int hidden, bool mfma) {
-  // x, its per-32 sums and the logit keys (and with MFMA gate/up units the B
+  // x and its per-32 sums (and with MFMA gate/up units the B
   // fragments, group sums and partial rows); or one batch of staged act
   // chunks and their sums
   const size_t xk = sizeof(float) * (size_t(nb) * hidden + size_t(nb) * (hidden / kChunk)) +
-                    sizeof(float) * kKeyFloats * nb +
                     (mfma ? size_t(kMG) * (1024 + 32) + sizeof(float) * kWaves * 128 : 0);
   const size_t st = sizeof(float) * (size_t(kStageFloats) * nb + size_t(8) * kSlotBatch * nb);
   return xk > st ? xk : st;
@@ -1432,7 +1430,7 @@ hipError_t launch_nb(LayerArgs &a, hipStream_t s) {
 template <int NB, int CPL>
 hipError_t launch_route_nb(LayerArgs &a, hipStream_t s) {
   const int H = a.l.hidden;
-  const size_t lds = sizeof(float) * (size_t(NB) * H + size_t(NB) * (H / kChunk) + size_t(kKeyFloats) * NB);
+  const size_t lds = sizeof(float) * (size_t(NB) * H + size_t(NB) * (H / kChunk));
   hipLaunchKernelGGL((route_kernel<NB, CPL>), dim3(a.route_blocks), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
