@@ -57,6 +57,10 @@ constexpr int kStagePad = 4;                          // floats after each stage
 // staged act floats per row of x: (slot groups x kSlotBatch) runs of W + pad, W >= 32
 constexpr int kStageFloats = kStageCols * kSlotBatch + (kStageCols / kChunk) * kSlotBatch * kStagePad;
 constexpr uint32_t kSpinLimit = 1u << 22;
+// x in LDS is chunk-major with rows of n_chunks + kXPad float4s: the pad
+// puts the 8 float4s of one chunk on different banks when they are written
+constexpr int kXPad = 1;
+__host__ __device__ constexpr int x_lds_floats(int nb, int hidden) { return nb * (hidden + 32 * kXPad); }
 
 struct LayerArgs {
   LayerLaunch l;
@@ -122,7 +126,7 @@ struct Shared {
 struct ChunkX {
   const float4 *p;
   int nch, c;
-  __device__ float4 operator()(int b, int q) const { return p[(b * 8 + q) * nch + c]; }
+  __device__ float4 operator()(int b, int q) const { return p[(b * 8 + q) * (nch + kXPad) + c]; }
 };
 
 template <int CPL>
@@ -1174,7 +1178,7 @@ __device__ __forceinline__ void stage_x(const LayerArgs &a, float *xs, float *xs
       const int i = threadIdx.x + t * kThreads;
       if (i * 4 < NB * H) {
         const int b = i / (H / 4), f = i - b * (H / 4);
-        reinterpret_cast<float4 *>(xs)[(b * 8 + f % 8) * nch + f / 8] = xv[t];
+        reinterpret_cast<float4 *>(xs)[(b * 8 + f % 8) * (nch + kXPad) + f / 8] = xv[t];
       }
     }
   }
@@ -1204,7 +1208,7 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
   // its down tiles after all of its gate/up units, so the act staging of the
   // down tiles reuses that space.
   float *xs = reinterpret_cast<float *>(dyn);           // [NB][H]
-  float *xsum = xs + NB * H;                            // [NB][H/32]
+  float *xsum = xs + x_lds_floats(NB, H);               // [NB][H/32]
   // MFMA gate/up operands after the sums: B fragments, group sums, the
   // waves' partial rows
   uint4 *xb = reinterpret_cast<uint4 *>(xsum + NB * (H / kChunk));
@@ -1229,8 +1233,11 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
     const int R = x < a.route_blocks ? (a.route_blocks - 1 - x) / a.n_slices + 1 : 0;
     RouterRow<CPL> rrow;
     if (route) router_prefetch<CPL>(a, g, rrow);
-    for (int e = threadIdx.x; e < a.l.n_experts; e += kThreads) rec_lds[e] = a.l.rec[e];
+    // the descriptors go to LDS after x is staged, so that no wait for them
+    // holds up the x loads (read after later barriers)
+    const uint64_t rv = a.l.rec[min(int(threadIdx.x), a.l.n_experts - 1)];
     stage_x<NB, CPL>(a, xs, xsum);
+    if (int(threadIdx.x) < a.l.n_experts) rec_lds[threadIdx.x] = rv;
 
     double *lg = a.l.slice_logits;
     float *gm = a.l.slice_gamma;
@@ -1354,7 +1361,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
   __shared__ uint64_t rec_lds[kMaxExperts];
   const int H = a.l.hidden;
   float *xs = reinterpret_cast<float *>(dyn);           // [NB][H]
-  float *xsum = xs + NB * H;                            // [NB][H/32]
+  float *xsum = xs + x_lds_floats(NB, H);               // [NB][H/32]
   if (threadIdx.x == 0) {
     const uint32_t e = ld_dev(a.l.sync + kSyncEpoch) + 1u;
     sh.ep = e ? e : 1u;
@@ -1362,9 +1369,9 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
   const int g = blockIdx.x;
   RouterRow<CPL> rrow;
   router_prefetch<CPL>(a, g, rrow);
-  if (g == 0)
-    for (int e = threadIdx.x; e < a.l.n_experts; e += kThreads) rec_lds[e] = a.l.rec[e];
+  const uint64_t rv = a.l.rec[min(int(threadIdx.x), a.l.n_experts - 1)];
   stage_x<NB, CPL>(a, xs, xsum);
+  if (g == 0 && int(threadIdx.x) < a.l.n_experts) rec_lds[threadIdx.x] = rv;   // read after the next barrier
   router_rows<NB, CPL>(a, xs, g, rrow, a.l.slice_logits, a.l.slice_gamma);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -1387,7 +1394,7 @@ size_t dyn_lds_bytes(int nb, int hidden, bool mfma) {
   // x and its per-32 sums (and with MFMA gate/up units the B
   // fragments, group sums and partial rows); or one batch of staged act
   // chunks and their sums
-  const size_t xk = sizeof(float) * (size_t(nb) * hidden + size_t(nb) * (hidden / kChunk)) +
+  const size_t xk = sizeof(float) * (size_t(x_lds_floats(nb, hidden)) + size_t(nb) * (hidden / kChunk)) +
                     (mfma ? size_t(kMG) * (1024 + 32) + sizeof(float) * kWaves * 128 : 0);
   const size_t st = sizeof(float) * (size_t(kStageFloats) * nb + size_t(8) * kSlotBatch * nb);
   return xk > st ? xk : st;
@@ -1430,7 +1437,7 @@ hipError_t launch_nb(LayerArgs &a, hipStream_t s) {
 template <int NB, int CPL>
 hipError_t launch_route_nb(LayerArgs &a, hipStream_t s) {
   const int H = a.l.hidden;
-  const size_t lds = sizeof(float) * (size_t(NB) * H + size_t(NB) * (H / kChunk));
+  const size_t lds = sizeof(float) * (size_t(x_lds_floats(NB, H)) + size_t(NB) * (H / kChunk));
   hipLaunchKernelGGL((route_kernel<NB, CPL>), dim3(a.route_blocks), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
