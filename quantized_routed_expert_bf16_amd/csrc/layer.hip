@@ -1161,27 +1161,67 @@ __device__ __forceinline__ void run_down_m(const LayerArgs &a, Shared<NB> &sh, i
 
 // The nb rows of x into LDS, chunk-major (ChunkX), and their per-32 sums.
 // All of a thread's loads are in flight at once.
+// An empty asm that takes every loaded value as a read-write register
+// operand: all of the loads are issued before it and nothing that uses them
+// moves above it (no memory clobber, so the values stay in registers).
+__device__ __forceinline__ void pin_loaded(floatx4 (&v)[2]) { asm volatile("" : "+v"(v[0]), "+v"(v[1])); }
+__device__ __forceinline__ void pin_loaded(floatx4 (&v)[4]) {
+  asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+}
+__device__ __forceinline__ void pin_loaded(floatx4 (&v)[6]) {
+  asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]));
+}
+__device__ __forceinline__ void pin_loaded(floatx4 (&v)[8]) {
+  asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
+               "+v"(v[7]));
+}
+__device__ __forceinline__ void pin_loaded(floatx4 (&v)[12]) {
+  asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
+               "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]));
+}
+__device__ __forceinline__ void pin_loaded(floatx4 (&v)[16]) {
+  asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
+               "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]),
+               "+v"(v[14]), "+v"(v[15]));
+}
+
+// The descriptor table (rec_dst, when not null: rv per thread) and the call's
+// epoch (ep_dst: the workspace's last epoch + 1, never 0) go to LDS together
+// with x, under the same barrier.
 template <int NB, int CPL>
-__device__ __forceinline__ void stage_x(const LayerArgs &a, float *xs, float *xsum) {
+__device__ __forceinline__ void stage_x(const LayerArgs &a, float *xs, float *xsum, uint64_t *rec_dst, uint64_t rv,
+                                        uint32_t *ep_dst) {
+  uint32_t ep_next = 0;
   const int H = a.l.hidden;
   {   // all of the thread's x loads in flight at once (H <= 2048 CPL)
     constexpr int kXIt = 2 * NB * CPL;
-    float4 xv[kXIt];
+    floatx4 xv[kXIt];
 #pragma unroll
     for (int t = 0; t < kXIt; ++t) {   // unconditional loads keep xv in registers
       const int i = min((threadIdx.x + t * kThreads) * 4, NB * H - 4);
-      xv[t] = *reinterpret_cast<const float4 *>(a.l.x + i);
+      xv[t] = *reinterpret_cast<const floatx4 *>(a.l.x + i);
     }
+    // the call's epoch, read by wave 0 (one device-coherent read per block)
+    // while the x loads are in flight
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0) ep_next = ld_dev(a.l.sync + kSyncEpoch) + 1u;
+    // every load ahead of the first write (left alone, the scheduler pairs
+    // each load with its write: one round trip per load)
+    pin_loaded(xv);
     const int nch = H / kChunk;
 #pragma unroll
     for (int t = 0; t < kXIt; ++t) {   // float4 f of row b -> group f % 8 of chunk f / 8
-      const int i = threadIdx.x + t * kThreads;
-      if (i * 4 < NB * H) {
-        const int b = i / (H / 4), f = i - b * (H / 4);
-        reinterpret_cast<float4 *>(xs)[(b * 8 + f % 8) * (nch + kXPad) + f / 8] = xv[t];
-      }
+      // unconditional writes (a guarded write lets the compiler sink its load
+      // into the branch, one round trip per load): past the rows, into the
+      // pad slot of the first LDS row, which is never read
+      const int i = threadIdx.x + t * kThreads, rq = H / 4;
+      const int b = int(i >= rq) + int(i >= 2 * rq) + int(i >= 3 * rq);   // row (nb <= 4), no division
+      const int f = i - b * rq;
+      const int at = i * 4 < NB * H ? (b * 8 + f % 8) * (nch + kXPad) + f / 8 : nch;
+      reinterpret_cast<floatx4 *>(xs)[at] = xv[t];
     }
   }
+  if (rec_dst && int(threadIdx.x) < a.l.n_experts) rec_dst[threadIdx.x] = rv;
+  if (threadIdx.x == 0) *ep_dst = ep_next ? ep_next : 1u;
   __syncthreads();
   for (int i = threadIdx.x; i < NB * (H / kChunk); i += kThreads) {   // per-32 sums
     const int b = i / (H / kChunk), c = i - b * (H / kChunk);
@@ -1219,12 +1259,9 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
 
   const int x = blockIdx.x % kSlices, lr = blockIdx.x / kSlices;
   const int P = a.per_slice;
-  // this call's epoch (tags the slice partials); never 0, the workspace's
-  // initial tag
-  if (threadIdx.x == 0) {
-    const uint32_t e = ld_dev(a.l.sync + kSyncEpoch) + 1u;
-    sh.ep = e ? e : 1u;
-  }
+  // this call's epoch (tags the slice partials; never 0, the workspace's
+  // initial tag) is read while x is staged (stage_x)
+
 
   if (x < a.n_slices) {
     // router blocks g < G are spread over the slices; R of them are in this one
@@ -1233,11 +1270,10 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
     const int R = x < a.route_blocks ? (a.route_blocks - 1 - x) / a.n_slices + 1 : 0;
     RouterRow<CPL> rrow;
     if (route) router_prefetch<CPL>(a, g, rrow);
-    // the descriptors go to LDS after x is staged, so that no wait for them
-    // holds up the x loads (read after later barriers)
+    // the descriptors go to LDS with x, so that no wait for them holds up
+    // the x loads
     const uint64_t rv = a.l.rec[min(int(threadIdx.x), a.l.n_experts - 1)];
-    stage_x<NB, CPL>(a, xs, xsum);
-    if (int(threadIdx.x) < a.l.n_experts) rec_lds[threadIdx.x] = rv;
+    stage_x<NB, CPL>(a, xs, xsum, rec_lds, rv, &sh.ep);
 
     double *lg = a.l.slice_logits;
     float *gm = a.l.slice_gamma;
@@ -1362,16 +1398,12 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerArgs a) {
   const int H = a.l.hidden;
   float *xs = reinterpret_cast<float *>(dyn);           // [NB][H]
   float *xsum = xs + x_lds_floats(NB, H);               // [NB][H/32]
-  if (threadIdx.x == 0) {
-    const uint32_t e = ld_dev(a.l.sync + kSyncEpoch) + 1u;
-    sh.ep = e ? e : 1u;
-  }
+
   const int g = blockIdx.x;
   RouterRow<CPL> rrow;
   router_prefetch<CPL>(a, g, rrow);
   const uint64_t rv = a.l.rec[min(int(threadIdx.x), a.l.n_experts - 1)];
-  stage_x<NB, CPL>(a, xs, xsum);
-  if (g == 0 && int(threadIdx.x) < a.l.n_experts) rec_lds[threadIdx.x] = rv;   // read after the next barrier
+  stage_x<NB, CPL>(a, xs, xsum, g == 0 ? rec_lds : nullptr, rv, &sh.ep);
   router_rows<NB, CPL>(a, xs, g, rrow, a.l.slice_logits, a.l.slice_gamma);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
