@@ -142,6 +142,33 @@ def test_full_shape_bad_descriptor(moe):
     assert moe.workspace_status(run.bufs.ws) == 0     # read-and-clear
 
 
+@pytest.mark.parametrize("shape", [
+    None,                                                    # full shape (H 2048, 128 experts, k 8)
+    dict(hidden=256, inter=128, n_experts=256, top_k=15),    # max experts and k
+    dict(hidden=4096, inter=256, n_experts=16, top_k=4),     # two chunks per lane
+    dict(hidden=768, inter=128, n_experts=1, top_k=1),       # single expert
+])
+@pytest.mark.parametrize("nb", [1, 2, 3, 4])
+def test_route_only_rows_and_shapes(moe, shape, nb):
+    """moe_route (the route-only kernel) writes the same routing tables as
+    moe_layer_forward, bit for bit, and they match the oracle's."""
+    if shape is None:
+        cfg = dataclasses.replace(syn.CONFIGS["verify_nb4"], x_mode="iid")
+        p = syn.make_problem(cfg, seed=7, device="cuda", n_layers=1)
+    else:
+        cfg = _small_cfg(**shape)
+        p = problem_to(syn.make_problem(cfg, seed=7, device="cpu"), "cuda")
+    run = DecodeRunner(moe, p)
+    x = _x(cfg, 40 + nb, nb, cfg.hidden, "cuda")
+    a = run.route(x, 0)
+    b = run.forward(x, 0)
+    for key in ("tab", "wmap", "ids", "topk_idx", "topk_w", "logits", "gamma"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+    r = oracle_layer(p, x.cpu().numpy(), 0)
+    compare_decode(b, r, cfg.top_k, f"route {shape} nb {nb}")
+    assert moe.workspace_status(run.bufs.ws) == 0
+
+
 def test_route_only_matches_forward(moe):
     cfg = syn.CONFIGS["verify_nb4"]
     p = syn.make_problem(cfg, seed=2, device="cuda", n_layers=1)
