@@ -51,7 +51,6 @@ constexpr int kPairsPerWave = kTileRowPairs / kWaves;
 constexpr int kRowsPerWave = 8;                       // down unit: 8 rows per wave
 constexpr int kRowsPerTile = kRowsPerWave * kWaves;   // 32 rows per down tile
 constexpr int kSlotBatch = 10;                        // slots per lane per down batch
-constexpr int kWaitVm0 = 0x0F70;                      // s_waitcnt vmcnt(0) only
 constexpr int kStageCols = 256;                       // slot groups x slice width (= 8 x 32)
 constexpr int kStagePad = 4;                          // floats after each staged (slot, row) run of W
 // staged act floats per row of x: (slot groups x kSlotBatch) runs of W + pad, W >= 32
@@ -1304,9 +1303,6 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
     const int slot0 = i / a.ups;
     const bool early = slot0 < a.l.top_k;
     uint64_t d0 = 0;
-    // retire every older vector memory access first, so that nothing in the
-    // union build has to wait on these loads
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     if (early) d0 = rec_lds[sh.sel[0][slot0]];
     if constexpr (kM) {
       // the block's units i, i + P, ... < n_gu run as a pipeline: the next
