@@ -61,11 +61,17 @@ constexpr bool frag_maps_inverse() {
 static_assert(frag_maps_inverse(), "frag_pos must invert frag_code");
 
 // ------------------------------------------------------------------ P1
-constexpr int kRouteTok = 4;   // rows per router block
+constexpr int kRouteTok = 4;     // rows per router block
+constexpr int kRouteSteps = 4;   // 512-input steps a lane has in flight (all of them at H = 2048)
 
-// Block (rb, tg): router rows 4 rb + wave (row E = shared gate) for rows
-// kRouteTok tg .. +kRouteTok, float64 accumulation; then every block takes a
-// share of the x -> f16 hi/lo split and the per-64 group sums.
+__host__ __device__ inline int pf_router_blocks(int n_experts, int t) {
+  return (n_experts + 1 + kWaves - 1) / kWaves * ((t + kRouteTok - 1) / kRouteTok);
+}
+
+// Blocks (rb, tg) below pf_router_blocks: router rows 4 rb + wave (row E =
+// shared gate) for rows kRouteTok tg .. +kRouteTok, float64 accumulation.
+// The blocks after them split x into f16 hi/lo halves and sum its 64-groups,
+// at the same time.
 __global__ __launch_bounds__(kThreads) void pf_router_kernel(PrefillArgs a, const uint16_t *router,
                                                              const uint16_t *gvec, double *logits,
                                                              float *gamma) {
@@ -77,11 +83,11 @@ __global__ __launch_bounds__(kThreads) void pf_router_kernel(PrefillArgs a, cons
   if (e <= E && r0 < t) {
     const uint16_t *w = e < E ? router + size_t(e) * H : gvec;
     double acc[kRouteTok] = {};
-    for (int i0 = lane * 8; i0 < H; i0 += 1024) {
-      uint4 wv[2];
-      float4 xv[2][kRouteTok][2];
+    for (int i0 = lane * 8; i0 < H; i0 += 512 * kRouteSteps) {
+      uint4 wv[kRouteSteps];
+      float4 xv[kRouteSteps][kRouteTok][2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {   // two 512-input steps in flight
+      for (int u = 0; u < kRouteSteps; ++u) {
         const int i = min(i0 + 512 * u, H - 8);
         wv[u] = *reinterpret_cast<const uint4 *>(w + i);
 #pragma unroll
@@ -92,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void pf_router_kernel(PrefillArgs a, cons
         }
       }
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < kRouteSteps; ++u) {
         if (i0 + 512 * u >= H) break;
         const float wf[8] = {bf16_lo(wv[u].x), bf16_hi(wv[u].x), bf16_lo(wv[u].y), bf16_hi(wv[u].y),
                              bf16_lo(wv[u].z), bf16_hi(wv[u].z), bf16_lo(wv[u].w), bf16_hi(wv[u].w)};
@@ -116,7 +122,10 @@ __global__ __launch_bounds__(kThreads) void pf_router_kernel(PrefillArgs a, cons
   }
   // x -> f16 hi/lo halves in both MFMA code orders: one 16-code block a
   // thread (4-bit order at xf[0], 2/3-bit order at xf[1])
-  for (int i0 = blockIdx.x * kThreads; i0 < t * H / 16; i0 += gridDim.x * kThreads) {
+  const int first_split = pf_router_blocks(E, t);
+  if (int(blockIdx.x) < first_split) return;
+  const int n_split = int(gridDim.x) - first_split;
+  for (int i0 = (int(blockIdx.x) - first_split) * kThreads; i0 < t * H / 16; i0 += n_split * kThreads) {
     // (t H / 16 is a multiple of 16, so whole 64-lane groups stay together)
     const int i = min(i0 + int(threadIdx.x), t * H / 16 - 1);
     const bool live = i0 + int(threadIdx.x) < t * H / 16;
@@ -700,7 +709,8 @@ hipError_t launch_prefill(const PrefillArgs &a, const uint16_t *router, const ui
     return hipSuccess;
   };
   hipError_t e;
-  const int route_blocks = (a.n_experts + 1 + kWaves - 1) / kWaves * ((a.t + kRouteTok - 1) / kRouteTok);
+  const int split_blocks = (a.t * a.hidden / 16 + kThreads - 1) / kThreads;
+  const int route_blocks = pf_router_blocks(a.n_experts, a.t) + split_blocks;
   hipLaunchKernelGGL(pf_router_kernel, dim3(route_blocks), dim3(kThreads), 0, s, a, router, gvec,
                      logits, gamma);
   if ((e = hipGetLastError()) != hipSuccess) return e;
