@@ -19,10 +19,10 @@ the rustdoc page "Struct Gpu", and the source pages gpu.rs and gpu/load.rs):
   descending logit; weights are the softmax over the k selected logits, i.e.
   the full softmax renormalised over the top-k (reading chosen because the
   pages leave renormalisation open).
-* Union and slot table (gpu.rs, ``union_of`` "unique entries in first-seen
-  order" over the row-major (row, rank) list; the ``slot_tab``/``wmap`` field
-  docs: 64 entries per layer, entry 62 = resident count, 63 = union size;
-  per-row routing weight per slot).
+* Union and slot table (gpu.rs, ``union_of``: the union keeps each expert
+  once, in the order it is first met walking the (row, rank) list row by row;
+  the ``slot_tab``/``wmap`` field docs: 64 entries per layer, entry 62 =
+  resident count, 63 = union size; per-row routing weight per slot).
 * Experts (Struct Gpu, ``experts_b``: routed experts of the union plus the
   shared expert, summed per row): a = silu(Wg x) * (Wu x), y = Wd a, with
   silu(g) = g / (1 + exp(-g)).

@@ -7,8 +7,10 @@ gate/up, a wrong nibble order, a transposed matrix, a lost tie rule) fails at
 least one of them; ``test_planted_mistakes_are_caught`` plants such slips in
 the oracle and checks that they are caught.
 """
+import inspect
 import math
 import os
+import textwrap
 
 import numpy as np
 import pytest
@@ -230,13 +232,18 @@ def test_union_slots_first_seen():
 
 # ---------------------------------------------------------------- layers --
 
-def test_golden_tiny_layer():
+def _golden_values(name):
     vals = {}
-    with open(os.path.join(GOLDEN, "tiny_layer.txt")) as f:
+    with open(os.path.join(GOLDEN, name)) as f:
         for line in f:
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=")
                 vals[k.strip()] = float(v)
+    return vals
+
+
+def test_golden_tiny_layer():
+    vals = _golden_values("tiny_layer.txt")
     H = I = 64
     pool = np.zeros(4 * syn.record_bytes(H, I, 4), dtype=np.uint8)
     s = _bf16(np.full((2 * I, 1), 2.0 ** -6))
@@ -260,6 +267,109 @@ def test_golden_tiny_layer():
     assert r["gamma"][0] == vals["gamma"]
     np.testing.assert_allclose(r["out_f64"][0], vals["out"], rtol=1e-15)
     assert abs(vals["out"] - 2.5 / (1 + math.exp(-1))) < 1e-15
+
+
+def _sig(v):
+    return 1.0 / (1.0 + math.exp(-v))
+
+
+def test_golden_tiny_layer_k2():
+    """Two routed experts per row and a non-zero shared gate vector
+    (tests/golden/tiny_layer_k2.txt): pins the routing-weighted combine at
+    k = 2 and the sign of the shared gate, through layer_forward and, for two
+    identical rows, prefill_forward."""
+    vals = _golden_values("tiny_layer_k2.txt")
+    # the stored numbers are the closed forms stated in the file
+    assert vals["out"] == pytest.approx(3 * _sig(1) ** 2 + 6 * _sig(-1) * _sig(2), rel=1e-15)
+    assert vals["weight0"] == pytest.approx(_sig(1), rel=1e-15)
+    assert vals["weight1"] == pytest.approx(_sig(-1), rel=1e-15)
+    assert vals["gamma"] == pytest.approx(_sig(1), rel=1e-15)
+    H = I = 64
+    rb = syn.record_bytes(H, I, 4)
+    pool = np.zeros(4 * rb, dtype=np.uint8)
+    s = _bf16(np.full((2 * I, 1), 2.0 ** -6))
+    sd = _bf16(np.full((H, 1), 2.0 ** -6))
+    z = _bf16(np.zeros((2 * I, 1)))
+    zd = _bf16(np.zeros((H, 1)))
+
+    def gu(gc, uc):
+        q = np.zeros((2 * I, H), dtype=np.int64)
+        q[0::2] = gc
+        q[1::2] = uc
+        return q
+
+    d0 = syn.write_record(pool, 0, H, I, 4, gu(1, 2), s, z, np.full((H, I), 1), sd, zd)
+    d1 = syn.write_record(pool, rb, H, I, 4, gu(2, 1), s, z, np.full((H, I), 3), sd, zd)
+    d2 = syn.write_record(pool, 2 * rb, H, I, 4, np.full((2 * I, H), 15), s, z,
+                          np.full((H, I), 15), sd, zd)
+    ds = syn.write_record(pool, 3 * rb, H, I, 4, gu(1, 1), s, z, np.full((H, I), 1), sd, zd)
+    router = _bf16(np.stack([np.full(H, 2.0 ** -6), np.zeros(H), np.full(H, -2.0 ** -6)]))
+    gvec = _bf16(np.full(H, 2.0 ** -6))
+    r = mo.layer_forward(np.ones((1, H), dtype=np.float32), router, [d0, d1, d2], pool, gvec,
+                         ds, 2, H, I)
+    np.testing.assert_array_equal(r["logits"][0], [vals["logit0"], vals["logit1"], vals["logit2"]])
+    np.testing.assert_array_equal(r["topk_idx"][0], [vals["expert0"], vals["expert1"]])
+    np.testing.assert_allclose(r["topk_w"][0], [vals["weight0"], vals["weight1"]], rtol=1e-15)
+    np.testing.assert_allclose(r["gamma"], [vals["gamma"]], rtol=1e-15)
+    np.testing.assert_allclose(r["out_f64"][0], vals["out"], rtol=1e-14)
+    p = mo.prefill_forward(np.ones((2, H), dtype=np.float32), router, [d0, d1, d2], pool, gvec,
+                           ds, 2, H, I)
+    np.testing.assert_allclose(p["topk_w"], [[vals["weight0"], vals["weight1"]]] * 2, rtol=1e-15)
+    np.testing.assert_allclose(p["out_f64"], vals["out"], rtol=1e-14)
+
+
+def _bf16_torch(v16):
+    """bf16 bit patterns -> float64 through torch (independent of the oracle)."""
+    t = torch.tensor(np.asarray(v16).astype(np.int32) << 16, dtype=torch.int32)
+    return t.view(torch.float32).double().numpy()
+
+
+def test_zero_scales_layer_closed_form():
+    """Every scale 0 in every record, so each weight row is its group biases
+    and an expert is a closed form in group sums: g = B_g xs, u = B_u xs,
+    y = B_d (group sums of silu(g) u).  The layer output over 4 rows with
+    k = 3 of 6 experts is then sum_r w_r y_{e_r} + gamma y_shared, with the
+    logits from a numpy product, top-k from lexsort, weights from
+    scipy.special.softmax and gamma from scipy.special.expit; it pins the
+    k >= 2 combine of layer_forward and prefill_forward."""
+    rng = np.random.default_rng(8)
+    H, I, E, k, nb = 256, 128, 6, 3, 4
+    rb = syn.record_bytes(H, I, 4)
+    pool = np.zeros((E + 1) * rb, dtype=np.uint8)
+    recs, descs = [], []
+    for e in range(E + 1):
+        r = _random_record(rng, H, I, 4, noise=0.05)
+        r["gu_s"] = _bf16(np.zeros(r["gu_s"].shape))
+        r["d_s"] = _bf16(np.zeros(r["d_s"].shape))
+        descs.append(_write(pool, e * rb, H, I, 4, r))
+        recs.append(r)
+    router = _bf16(0.3 * rng.standard_normal((E, H)))
+    gvec = _bf16(0.05 * rng.standard_normal(H))
+    x = _rms_rows(rng, nb, H)
+    xd = x.astype(np.float64)
+    logits = xd @ _bf16_torch(router).T
+    gam = scipy.special.expit(xd @ _bf16_torch(gvec))
+
+    def expert_out(r, xb):
+        xs = xb.reshape(-1, 64).sum(axis=1)
+        gb = _bf16_torch(r["gu_b"])
+        g, u = gb[0::2] @ xs, gb[1::2] @ xs
+        a = g * scipy.special.expit(g) * u
+        return _bf16_torch(r["d_b"]) @ a.reshape(-1, 64).sum(axis=1)
+
+    expect = np.zeros((nb, H))
+    for b in range(nb):
+        top = np.lexsort((np.arange(E), -logits[b]))[:k]
+        w = scipy.special.softmax(logits[b, top])
+        assert w.min() < 0.9 * w.max()      # weights that matter
+        for wr, e in zip(w, top):
+            expect[b] += wr * expert_out(recs[e], xd[b])
+        expect[b] += gam[b] * expert_out(recs[E], xd[b])
+    atol = 1e-12 * np.abs(expect).max()
+    res = mo.layer_forward(x, router, descs[:E], pool, gvec, descs[E], k, H, I)
+    np.testing.assert_allclose(res["out_f64"], expect, rtol=1e-11, atol=atol)
+    pre = mo.prefill_forward(x, router, descs[:E], pool, gvec, descs[E], k, H, I)
+    np.testing.assert_allclose(pre["out_f64"], expect, rtol=1e-11, atol=atol)
 
 
 @pytest.mark.parametrize("bits", [4, 3, 2])
@@ -364,12 +474,29 @@ def _planted(monkeypatch, name, fn):
     monkeypatch.setattr(mo, name, fn)
 
 
+def _edited(fn, old, new):
+    """fn recompiled from its own source with one expression replaced (a
+    mistake planted inside the function body)."""
+    src = textwrap.dedent(inspect.getsource(fn))
+    assert src.count(old) == 1, f"{old!r} not found once in {fn.__name__}"
+    ns = {}
+    exec(compile(src.replace(old, new), inspect.getsourcefile(fn), "exec"), fn.__globals__, ns)
+    return ns[fn.__name__]
+
+
+LAYER_COMBINE = 'acc[b] += slots["wmap"][b, j] * y'
+PREFILL_COMBINE = 'acc[r_] += csr["wts"][p] * y'
+
+
 @pytest.mark.parametrize("mistake", ["nibble_order", "swap_gate_up", "drop_bias",
                                      "tie_to_higher_id", "no_renormalise", "transpose_down",
-                                     "gamma_without_sigmoid", "union_sorted"])
+                                     "gamma_without_sigmoid", "union_sorted",
+                                     "combine_drops_weight", "layer_combine_drops_weight",
+                                     "prefill_combine_drops_weight", "gate_sign"])
 def test_planted_mistakes_are_caught(monkeypatch, mistake):
     orig = {n: getattr(mo, n) for n in ("unpack_codes", "read_expert", "dequant",
-                                        "topk_softmax", "union_slots", "shared_gate")}
+                                        "topk_softmax", "union_slots", "shared_gate",
+                                        "layer_forward", "prefill_forward")}
     if mistake == "nibble_order":
         def bad(packed, n, bits):
             c = orig["unpack_codes"](packed, n, bits)
@@ -421,6 +548,21 @@ def test_planted_mistakes_are_caught(monkeypatch, mistake):
             return s
         _planted(monkeypatch, "union_slots", bad)
         checks = [test_union_slots_first_seen]
+    elif mistake in ("combine_drops_weight", "layer_combine_drops_weight",
+                     "prefill_combine_drops_weight"):
+        # the routing weight left out of the combine, in one function or both
+        if mistake != "prefill_combine_drops_weight":
+            _planted(monkeypatch, "layer_forward",
+                     _edited(orig["layer_forward"], LAYER_COMBINE, "acc[b] += y"))
+        if mistake != "layer_combine_drops_weight":
+            _planted(monkeypatch, "prefill_forward",
+                     _edited(orig["prefill_forward"], PREFILL_COMBINE, "acc[r_] += y"))
+        checks = [test_golden_tiny_layer_k2, test_zero_scales_layer_closed_form]
+    elif mistake == "gate_sign":
+        def bad(x, gvec):
+            return mo.sigmoid(-(np.asarray(x, dtype=np.float64) @ mo.bf16_to_f64(gvec)))
+        _planted(monkeypatch, "shared_gate", bad)
+        checks = [test_golden_tiny_layer_k2, test_zero_scales_layer_closed_form]
     for check in checks:
         with pytest.raises(AssertionError):
             check()
