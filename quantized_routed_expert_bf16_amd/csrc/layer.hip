@@ -1367,6 +1367,11 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
     } else {
       for (; i < n_total; i += P) run_down<NB>(a, sh, x, i - n_gu, act_lds, asum_lds);
     }
+  } else if (threadIdx.x == 0) {
+    // a block of a slice without columns (I < 8 * 32) still reads the call's
+    // epoch: whichever block leaves last publishes its copy
+    const uint32_t e = ld_dev(a.l.sync + kSyncEpoch) + 1u;
+    sh.ep = e ? e : 1u;
   }
 
   // two-level exit count; the last block out resets the counters

@@ -9,7 +9,8 @@ import torch
 
 import oracle.moe_oracle as mo
 import synthetic as syn
-from gpu_support import (DecodeRunner, PoolView, compare_decode, oracle_layer, problem_to, u16)
+from gpu_support import (DecodeRunner, PoolView, compare_decode, dyadic_router, dyadic_x,
+                         exact_logits, oracle_layer, problem_to, u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,8 +51,7 @@ def test_tiny_layer(moe, nb, seed):
     x = _x(cfg, seed, nb, cfg.hidden, "cuda")
     g = run.forward(x, 0)
     r = oracle_layer(p, x.cpu().numpy(), 0)
-    st = compare_decode(g, r, cfg.top_k, f"tiny seed {seed} nb {nb}")
-    assert st["ambiguous"] == 0
+    compare_decode(g, r, cfg.top_k, f"tiny seed {seed} nb {nb}")
     assert moe.workspace_status(run.bufs.ws) == 0
 
 
@@ -214,3 +214,114 @@ def test_bad_descriptor_is_skipped_and_flagged(moe):
     err = np.abs(g["out"][0] - expect).max()
     assert err <= 1e-3 * np.abs(expect).max()
     assert moe.workspace_status(run.bufs.ws) == 0     # read-and-clear
+
+
+# ---------------------------------------------------------------- exact ties
+# Router inputs rounded so that every logit is exact on both sides (see
+# gpu_support.dyadic_x): equal router rows give bit-equal logits, so the
+# top-k, the union and the slot table are decided by the tie rule (logit
+# descending, lower expert id first) and must match the oracle bit for bit.
+
+def _tie_problem(shape):
+    if shape is None:
+        cfg = dataclasses.replace(syn.CONFIGS["verify_nb4"], x_mode="iid")
+        p = syn.make_problem(cfg, seed=12, device="cuda", n_layers=1)
+    else:
+        cfg = _small_cfg(**shape)
+        p = problem_to(syn.make_problem(cfg, seed=12, device="cpu"), "cuda")
+    router = p.router.clone()
+    router[0] = dyadic_router(router[0])
+    return cfg, dataclasses.replace(p, router=router)
+
+
+def tie_case(case, cfg, p, x):
+    """Router of layer 0 rewritten for one tie case; returns (router, expect),
+    expect = (lower id that must be selected, higher id that must not) or None."""
+    E, k = cfg.n_experts, cfg.top_k
+    R = p.router[0].clone()
+    expect = None
+    if case in ("straddle_lower", "straddle_higher"):
+        # a copy of the k-th expert's row (row 0 of x) at another id: the two
+        # tie across the k boundary and the lower id takes the place
+        lg = exact_logits(x[:1], R)[0]
+        order = np.lexsort((np.arange(E), -lg))
+        ek = int(order[k - 1])
+        if case == "straddle_lower":
+            cands = [int(e) for e in order[k:] if e < ek]
+        else:
+            cands = [int(e) for e in order[k:] if e > ek]
+        if not cands:
+            pytest.skip(f"no expert id on that side of {ek}")
+        other = cands[0]
+        R[other] = R[ek]
+        expect = (min(ek, other), max(ek, other))
+    elif case == "signed_zeros":
+        # x > 0 (dyadic_x(positive=True)); zero rows, alternately +0 and -0
+        # bit patterns, give logits of +-0 that tie with each other; every
+        # other row is a distinct negative constant, below them
+        zero_ids = list(range(1, E, max(1, E // (k + 3))))[: k + 2]
+        for e in range(E):
+            R[e] = -float((1 + e % 200)) / 2048.0
+        for i, e in enumerate(zero_ids):
+            R[e] = -0.0 if i % 2 else 0.0
+    elif case == "all_equal":
+        R[:] = R[0]
+    else:
+        raise ValueError(case)
+    return R.contiguous(), expect
+
+
+TIE_CASES = ["straddle_lower", "straddle_higher", "signed_zeros", "all_equal"]
+
+
+@pytest.mark.parametrize("shape", [None, dict(hidden=256, inter=128, n_experts=256, top_k=15)])
+@pytest.mark.parametrize("nb", [1, 4])
+@pytest.mark.parametrize("case", TIE_CASES)
+def test_exact_ties(moe, shape, nb, case):
+    cfg, p = _tie_problem(shape)
+    _say(f"[ties] {case} shape={shape} nb={nb}")
+    x = dyadic_x(_x(cfg, 50 + nb, nb, cfg.hidden, "cpu"), positive=case == "signed_zeros").cuda()
+    R, expect = tie_case(case, cfg, p, x.cpu())
+    router = p.router.clone()
+    router[0] = R
+    p = dataclasses.replace(p, router=router)
+    lg = exact_logits(x.cpu(), R)
+    assert any(len(set(lg[b])) < cfg.n_experts for b in range(nb))   # ties are there
+    run = DecodeRunner(moe, p)
+    g = run.forward(x, 0)
+    r = oracle_layer(p, x.cpu().numpy(), 0)
+    np.testing.assert_array_equal(g["logits"], lg)   # exact on the device too
+    compare_decode(g, r, cfg.top_k, f"ties {case} {shape} nb {nb}")
+    a = run.route(x, 0)
+    for key in ("tab", "wmap", "ids", "topk_idx", "topk_w"):
+        np.testing.assert_array_equal(a[key], g[key], err_msg=key)
+    if expect is not None:
+        assert expect[0] in g["topk_idx"][0] and expect[1] not in g["topk_idx"][0]
+    if case == "all_equal":
+        for b in range(nb):
+            np.testing.assert_array_equal(g["topk_idx"][b], np.arange(cfg.top_k))
+        np.testing.assert_array_equal(g["ids"][: cfg.top_k], np.arange(cfg.top_k))
+        np.testing.assert_allclose(g["topk_w"], 1.0 / cfg.top_k, rtol=1e-6)
+    assert moe.workspace_status(run.bufs.ws) == 0
+
+
+@pytest.mark.parametrize("inter", [64, 128])
+def test_epoch_advances_once_per_call(moe, inter):
+    """With I < 256 some slices of the decode grid have no columns; every
+    block still reads the call's epoch, so the workspace epoch word goes up
+    by exactly one per call whichever block leaves last."""
+    cfg = _small_cfg(hidden=256, inter=inter, n_experts=8, top_k=2)
+    p = problem_to(syn.make_problem(cfg, seed=9, device="cpu"), "cuda")
+    run = DecodeRunner(moe, p)
+    x = _x(cfg, 9, 2, cfg.hidden, "cuda")
+    ep_word = run.bufs.ws.view(torch.int32)
+    first = run.forward(x, 0)
+    prev = int(ep_word[608].item())
+    for i in range(60):
+        g = run.forward(x, 0)
+        now = int(ep_word[608].item())
+        assert now == prev + 1, f"call {i}: epoch {prev} -> {now}"
+        prev = now
+        np.testing.assert_array_equal(g["out"], first["out"])
+    compare_decode(first, oracle_layer(p, x.cpu().numpy(), 0), cfg.top_k, f"epoch I={inter}")
+    assert moe.workspace_status(run.bufs.ws) == 0

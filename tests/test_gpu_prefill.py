@@ -9,7 +9,9 @@ import torch
 
 import oracle.moe_oracle as mo
 import synthetic as syn
-from gpu_support import OUT_TOL, WEIGHT_RTOL, PoolView, problem_to, topk_gap, u16
+from gpu_support import (OUT_TOL, WEIGHT_RTOL, PoolView, assert_no_near_ties, dyadic_x,
+                         exact_logits, problem_to, u16)
+from test_gpu_decode import TIE_CASES, _tie_problem, tie_case
 
 pytestmark = pytest.mark.gpu
 
@@ -69,8 +71,7 @@ def _compare(g, r, k, what):
     for b in range(t):
         idx, _ = mo.topk_softmax(g["logits"][b], k)
         np.testing.assert_array_equal(g["topk_idx"][b], idx, err_msg=what)
-    ambiguous = sum(topk_gap(r["logits"][b], k) < 1e-9 for b in range(t))
-    assert ambiguous == 0, what
+    assert_no_near_ties(r["logits"], k, what)
     np.testing.assert_array_equal(g["topk_idx"], r["topk_idx"], err_msg=what)
     np.testing.assert_allclose(g["topk_w"], r["topk_w"], rtol=WEIGHT_RTOL, atol=0, err_msg=what)
     np.testing.assert_allclose(g["gamma"], r["gamma"], rtol=1e-6, err_msg=what)
@@ -154,3 +155,31 @@ def test_prefill_deterministic(moe):
         b = run.forward(x, 0)
         for key in a:
             np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+
+
+@pytest.mark.parametrize("shape", [None, dict(hidden=256, inter=128, n_experts=256, top_k=15)])
+@pytest.mark.parametrize("t", [5, 32])
+@pytest.mark.parametrize("case", TIE_CASES)
+def test_prefill_exact_ties(moe, shape, t, case):
+    """Exact logit ties in a prefill chunk: the top-k of every row, the CSR
+    grouping and the outputs match the oracle bit for bit (ids) under the
+    lower-id rule."""
+    cfg, p = _tie_problem(shape)
+    _say(f"[prefill ties] {case} shape={shape} t={t}")
+    g0 = torch.Generator().manual_seed(60 + t)
+    x = torch.randn(t, cfg.hidden, generator=g0)
+    x = dyadic_x(x / torch.sqrt((x * x).mean(dim=1, keepdim=True)), positive=case == "signed_zeros")
+    R, expect = tie_case(case, cfg, p, x)
+    router = p.router.clone()
+    router[0] = R
+    p = dataclasses.replace(p, router=router)
+    run = PrefillRunner(moe, p)
+    g = run.forward(x.cuda(), 0)
+    r = _oracle(p, x.numpy(), 0)
+    np.testing.assert_array_equal(g["logits"], exact_logits(x, R))
+    _compare(g, r, cfg.top_k, f"prefill ties {case} {shape} t={t}")
+    if expect is not None:
+        assert expect[0] in g["topk_idx"][0] and expect[1] not in g["topk_idx"][0]
+    if case == "all_equal":
+        np.testing.assert_array_equal(g["topk_idx"], np.tile(np.arange(cfg.top_k), (t, 1)))
+    assert moe.workspace_status(run.bufs.ws) == 0
