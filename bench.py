@@ -68,6 +68,61 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def host_info():
+    """Host cores and CPU model of the machine the bench runs on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
+    return {"nproc": os.cpu_count(), "affinity_cpus": affinity, "cpu_model": model}
+
+
+def blas_threads():
+    try:
+        import threadpoolctl
+        return max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    except Exception:
+        return None
+
+
+def gpu_state():
+    """Clock and temperature of the GPU from rocm-smi (a separate process);
+    None where the tool is missing or its output has no such field."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showtemp", "--showclocks", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        data = json.loads(r.stdout)
+    except Exception as e:   # tool missing or no JSON: record why
+        return {"error": str(e)[:200]}
+    card = next((v for k, v in data.items() if k.startswith("card")), {})
+    keep = {}
+    for k, v in card.items():
+        kl = k.lower()
+        if "temperature" in kl or "sclk" in kl or "mclk" in kl or "fclk" in kl:
+            keep[k] = v
+    return keep
+
+
+def check_status(moe, ws, what):
+    """The workspace status word after a pass: any bit set means a kernel
+    skipped a record (bit 0) or a bounded wait ran out (bit 2, output not
+    valid); the bench line is then not a valid measurement."""
+    st = moe.workspace_status(ws)
+    if st:
+        raise SystemExit(f"{what}: workspace status {st:#x} after the timed pass "
+                         "(bit 0: bad descriptor skipped; bit 2: a bounded wait ran out)")
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -80,6 +135,8 @@ def parse():
     ap.add_argument("--chunk", type=int, default=25, help="steps per captured graph")
     ap.add_argument("--stage-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds-extra", type=float, default=6.0,
+                    help="oracle seconds (timing + parity sample) per extra configuration; 0 = none")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="N",
@@ -444,11 +501,13 @@ def bench_prefill(moe, torch, syn, name, args):
     cnt, all_b, gu_b, flops = b.costs(ptrs)
     log(f"{name}: timed pass (graph)")
     total_ms = b.run_graph()
+    check_status(moe, b.bufs.ws, f"{name} timed pass")
     n_calls = cfg.steps * b.L
     us_call = total_ms * 1e3 / n_calls
     total_s = total_ms / 1e3
     log(f"{name}: {us_call:.2f} us per chunk-layer, {all_b.sum() / total_s / 1e9:.0f} GB/s")
     n_st, per = b.stage_pass(4)
+    check_status(moe, b.bufs.ws, f"{name} stage pass")
     gu_us = statistics.mean(per["gate_up"])
     gu_gbs = float(gu_b[:n_st].mean()) / (gu_us * 1e-6) / 1e9
     down_us = statistics.mean(per["down"])
@@ -470,6 +529,8 @@ def bench_prefill(moe, torch, syn, name, args):
         "gate_up_tflops": float(flops[:n_st].mean() * 2 / 3 / (gu_us * 1e-6) / 1e12),
         "down_us_mean": down_us,
     }
+    if args.cpu_seconds_extra > 0:
+        out["cpu"] = cpu_baseline_prefill(b, args.cpu_seconds_extra)
     del b
     torch.cuda.empty_cache()
     return out
@@ -489,7 +550,9 @@ def bench_decode(moe, torch, syn, name, args, with_cpu):
     u, expert_b, all_b, _ = b.bytes_of(tabs)
     log(f"{name}: timed pass ({args.mode})")
     if args.mode == "graph":
-        per_step, _, wall, total_ms = b.run_graph(args.chunk)
+        # at least four timed replays, so that the p90 is a real one
+        chunk = max(1, min(args.chunk, args.steps // 4))
+        per_step, _, wall, total_ms = b.run_graph(chunk)
     else:
         per_step, _, wall = b.run_eager()
         total_ms = sum(per_step)
@@ -499,8 +562,10 @@ def bench_decode(moe, torch, syn, name, args, with_cpu):
     expert_gbs = expert_b.sum() / total_s / 1e9
     all_gbs = all_b.sum() / total_s / 1e9
     log(f"{name}: {statistics.median(us_layer):.2f} us/layer, expert {expert_gbs:.0f} GB/s")
+    check_status(moe, b.bufs.ws, f"{name} timed pass")
     log(f"{name}: stage pass")
     n_st, layer_us = b.stage_pass(args.stage_steps)
+    check_status(moe, b.bufs.ws, f"{name} stage pass")
     # the timed region launches exactly one layer kernel per (step, layer) on
     # one stream, so its event time / launches is the kernel's mean duration
     k_us = total_ms * 1e3 / (L * args.steps)
@@ -525,34 +590,60 @@ def bench_decode(moe, torch, syn, name, args, with_cpu):
         "stage_steps": n_st,
         "kernel_bytes_per_launch_mean": float(np.mean(k_bytes)),
         "kernel_gbs": k_gbs,
+        "timed_samples": len(per_step),
         "wall_s": wall,
     }
     if with_cpu:
         out["cpu"] = cpu_baseline(b, args.cpu_seconds)
+    elif args.cpu_seconds_extra > 0:
+        out["cpu"] = cpu_baseline(b, args.cpu_seconds_extra)
     del b
     torch.cuda.empty_cache()
     return out
 
 
+class _PoolSlices:
+    """Byte slices of the device pool, copied to the host when the oracle
+    reads a record (no host copy of the whole pool)."""
+
+    def __init__(self, pool):
+        self.pool = pool
+
+    def __getitem__(self, sl):
+        return self.pool[sl].cpu().numpy()
+
+
+PARITY_TOL = 1e-3   # max-abs error <= 1e-3 * max|out| per layer (the parity bar)
+
+
+def _parity(refs, gpu, what):
+    import numpy as np
+    rel, ids_exact = 0.0, True
+    for r, g in zip(refs, gpu):
+        ref = r["out_f64"]
+        rel = max(rel, float(np.abs(g["out"] - ref).max() / np.abs(ref).max()))
+        if "ids" in g:
+            ids_exact &= bool(np.array_equal(g["ids"].view(np.uint32), r["ids"]))
+        if "ptr" in g:
+            ids_exact &= bool(np.array_equal(g["ptr"], r["ptr"]))
+            ids_exact &= bool(np.array_equal(g["rows"], r["rows"]))
+    if not ids_exact or rel > PARITY_TOL:
+        raise SystemExit(f"{what}: parity sample failed (ids exact {ids_exact}, max err / max|out| {rel:.2e})")
+    return rel, ids_exact
+
+
 def cpu_baseline(b, seconds):
-    """The float64 oracle on the host, on the first layers of the first timed step."""
+    """The float64 oracle on the host, on the first layers of the first timed
+    step, with parity of those layers asserted."""
     import numpy as np
     import oracle.moe_oracle as mo
     c = b.cfg
-    log(f"cpu baseline: copying the pool to the host")
-    pool = b.p.pool.cpu().numpy()
+    pool = _PoolSlices(b.p.pool)
     routers = b.p.router.view(b.torch.int16).cpu().numpy().view(np.uint16)
     gates = b.p.shared_gate.view(b.torch.int16).cpu().numpy().view(np.uint16)
     rec = b.p.rec.cpu().numpy()
     srec = b.p.shared_rec.cpu().numpy()
     x = b.x[b.warmup].cpu().numpy()
-    threads = None
-    try:
-        import threadpoolctl
-        threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
-    except Exception:
-        threads = 1
-    gpu = None
     t_total = 0.0
     n = 0
     refs = []
@@ -564,22 +655,55 @@ def cpu_baseline(b, seconds):
         refs.append(r)
         n += 1
     gpu = b.snapshot_layers(0, n)
-    # parity of the sampled layers (same seeded inputs)
-    rel, ids_exact = 0.0, True
+    rel, ids_exact = _parity(refs, gpu, f"{c.name} cpu baseline")
     expert_bytes = 0
-    for r, g in zip(refs, gpu):
-        ref = r["out_f64"]
-        rel = max(rel, float(np.abs(g["out"] - ref).max() / np.abs(ref).max()))
-        ids_exact &= bool(np.array_equal(g["ids"].view(np.uint32), r["ids"]))
+    for r in refs:
         u = r["n_union"]
         expert_bytes += sum(b.moe.record_bytes(c.hidden, c.inter, {0: 4, 1: 3, 2: 2}[int(d) & 3])
                             for d in r["tab"][:u]) + b.moe.record_bytes(c.hidden, c.inter, 4)
-    log(f"cpu baseline: {n} layers in {t_total:.1f} s; parity max rel err {rel:.2e} ids exact {ids_exact}")
-    return {"value": expert_bytes / t_total / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "us_per_layer": t_total / n * 1e6,
+    log(f"cpu baseline {c.name}: {n} layers in {t_total:.1f} s; parity max rel err {rel:.2e} "
+        f"ids exact {ids_exact}")
+    return {"value": expert_bytes / t_total / 1e9, "unit": "GB/s", "cores": blas_threads(),
+            "kind": "oracle", "us_per_layer": t_total / n * 1e6,
+            "host": host_info(),
             "sample": f"{c.name}: first {n} layers of timed step 0 (same seeded inputs), "
-                      f"float64 numpy oracle, host pool copy excluded",
+                      f"float64 numpy oracle (BLAS threads = cores), records read from the "
+                      f"device pool as the oracle needs them (copy time included)",
             "parity_sampled": {"layers": n, "max_err_over_absmax": rel, "ids_exact": ids_exact}}
+
+
+def cpu_baseline_prefill(b, seconds):
+    """The oracle's prefill_forward on the first layers of the first timed
+    chunk, with parity (CSR bit-exact, outputs within the bar) asserted."""
+    import numpy as np
+    import oracle.moe_oracle as mo
+    c = b.cfg
+    pool = _PoolSlices(b.p.pool)
+    routers = b.p.router.view(b.torch.int16).cpu().numpy().view(np.uint16)
+    gates = b.p.shared_gate.view(b.torch.int16).cpu().numpy().view(np.uint16)
+    rec = b.p.rec.cpu().numpy()
+    srec = b.p.shared_rec.cpu().numpy()
+    x = b.x[b.warmup].cpu().numpy()
+    t_total, n, refs, gpu = 0.0, 0, [], []
+    st = b.torch.cuda.current_stream().cuda_stream
+    while n < b.L and (t_total < seconds or n == 0):
+        t0 = time.perf_counter()
+        r = mo.prefill_forward(x[n], routers[n], rec[n], pool, gates[n], int(srec[n]), c.top_k,
+                               c.hidden, c.inter)
+        t_total += time.perf_counter() - t0
+        refs.append(r)
+        b.call(b.warmup, n, st)
+        b.torch.cuda.synchronize()
+        k = c.top_k
+        gpu.append({"out": b.out[n].cpu().numpy().copy(),
+                    "ptr": b.bufs.expert_ptr.cpu().numpy().copy(),
+                    "rows": b.bufs.entry_row[: b.t * k].cpu().numpy().copy()})
+        n += 1
+    rel, exact = _parity(refs, gpu, f"{c.name} cpu baseline")
+    log(f"cpu baseline {c.name}: {n} chunk-layers in {t_total:.1f} s; parity max rel err {rel:.2e}")
+    return {"us_per_chunk_layer": t_total / n * 1e6, "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{c.name}: first {n} layers of timed chunk 0, float64 numpy oracle",
+            "parity_sampled": {"layers": n, "max_err_over_absmax": rel, "csr_exact": exact}}
 
 
 def main():
@@ -603,6 +727,9 @@ def main():
         torch.cuda.synchronize()
         log(f"copy probe: {args.copy_probe} x neg over {4 * n} bytes")
         del src, dst
+    if args.no_cpu:
+        args.cpu_seconds_extra = 0.0
+    gpu_before = gpu_state()
     main_res = bench_decode(moe, torch, syn, args.config, args, with_cpu=not args.no_cpu)
     extra = {}
     for name in [n for n in args.extra.split(",") if n]:
@@ -610,6 +737,7 @@ def main():
             extra[name] = bench_prefill(moe, torch, syn, name, args)
         else:
             extra[name] = bench_decode(moe, torch, syn, name, args, with_cpu=False)
+    gpu_after = gpu_state()
     line = {
         "metric": METRIC,
         "value": round(main_res["expert_weight_gbs"], 2),
@@ -636,6 +764,8 @@ def main():
                      "bytes_per_launch": round(main_res["kernel_bytes_per_launch_mean"]),
                      "us_per_launch": round(main_res["kernel_us_mean"], 3)},
         "cpu_baseline": main_res.get("cpu"),
+        "host": host_info(),
+        "gpu_state": {"before": gpu_before, "after": gpu_after},
         "detail": main_res,
         "extra": extra,
     }

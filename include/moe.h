@@ -141,7 +141,15 @@ typedef struct moe_prefill_plan {
 uint64_t moe_record_bytes(int32_t hidden, int32_t inter, int32_t bits);
 
 /* Workspace bytes for up to max_rows rows (1..4 decode, 1..32 prefill);
- * 0 if dims or max_rows are invalid. */
+ * 0 if dims or max_rows are invalid.  The analog of the engine's expert
+ * scratch, which the gpu/load.rs source page (load_bounded, the Scratch
+ * buffers) sizes once for MAX_NB rows and k * MAX_NB + 1 union entries (the
+ * routed union plus the shared expert): here the per-call exchange of the
+ * decode kernel (counters, act values of up to 64 slots x 4 rows, per-slice
+ * partial outputs, router logits) and the prefill buffers for max_rows rows
+ * (MFMA-ordered x, act per (row, rank) entry, weighted outputs).  The
+ * caller allocates it (device memory, 256-byte aligned) and keeps it for
+ * the calls that use it; one workspace serves one stream at a time. */
 size_t moe_workspace_bytes(const moe_dims *dims, int32_t max_rows);
 
 /* Zero-fill a workspace on `stream` (a fill kernel, no memset node). */
@@ -184,7 +192,11 @@ int moe_workspace_status(void *ws, size_t ws_bytes, void *stream);
  * hook off.  No work is skipped.  At most 8 events. */
 int moe_set_stage_events(void *const *events, int32_t n);
 
-/* Text of the last non-zero return on the calling thread ("" if none). */
+/* Text of the last non-zero return on the calling thread ("" if none): the
+ * analog of the error messages of the shape checks in load_bounded (gpu/load.rs
+ * source page, e.g. the check that k * MAX_NB entries leave room in the
+ * 64-entry slot table) and of the HIP error of a failed launch.  The returned
+ * string is owned by the library and valid until the thread's next call. */
 const char *moe_last_error(void);
 
 #ifdef __cplusplus

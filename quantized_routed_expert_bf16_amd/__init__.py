@@ -22,6 +22,8 @@ RESIDENT_ENTRY = 62
 UNION_ENTRY = 63
 MAX_PREFILL_ROWS = 32
 OK, EINVAL, EWORKSPACE, ELAUNCH = 0, -1, -2, -3
+STATUS_BAD_RECORD = 1     # a record descriptor outside the pool (or tag 3) was skipped
+STATUS_WAIT_RAN_OUT = 4   # a bounded cross-block wait ran out: the output is not valid
 
 
 class MoeError(RuntimeError):
@@ -131,23 +133,45 @@ def workspace_init(ws: torch.Tensor, stream=None) -> None:
     _check(lib.moe_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def route(x, nb: int, router: MoeRouter, shared: MoeShared, slots: MoeSlots, stream=None) -> None:
+def _status_checked(ws_ptr: int, ws_bytes: int, stream) -> None:
+    """Synchronise the stream, read and clear the workspace status word and
+    raise if the call skipped a record or a bounded wait ran out."""
+    st = _check(lib.moe_workspace_status(ws_ptr, ws_bytes, _stream(stream)))
+    if st & STATUS_WAIT_RAN_OUT:
+        raise MoeError(ELAUNCH, f"status {st:#x}: a bounded wait between blocks ran out "
+                                "(another workload held the GPU); the output is not valid")
+    if st & STATUS_BAD_RECORD:
+        raise MoeError(EINVAL, f"status {st:#x}: a record descriptor outside the pool was skipped")
+
+
+def route(x, nb: int, router: MoeRouter, shared: MoeShared, slots: MoeSlots, stream=None,
+          check: bool = False) -> None:
+    """moe_route.  check=True synchronises and raises on a non-zero status."""
     _check(lib.moe_route(_ptr(x), nb, ctypes.byref(router), ctypes.byref(shared),
                          ctypes.byref(slots), _stream(stream)))
+    if check:
+        _status_checked(slots.ws, slots.ws_bytes, stream)
 
 
 def layer_forward(x, nb: int, router: MoeRouter, slots: MoeSlots, pool: MoePool,
-                  shared: MoeShared, out, stream=None) -> None:
+                  shared: MoeShared, out, stream=None, check: bool = False) -> None:
+    """moe_layer_forward.  check=True synchronises and raises on a non-zero
+    status (the checked mode for callers that may share the GPU)."""
     _check(lib.moe_layer_forward(_ptr(x), nb, ctypes.byref(router), ctypes.byref(slots),
                                  ctypes.byref(pool), ctypes.byref(shared), _ptr(out),
                                  _stream(stream)))
+    if check:
+        _status_checked(slots.ws, slots.ws_bytes, stream)
 
 
 def prefill_forward(x, t: int, router: MoeRouter, plan: MoePrefillPlan, pool: MoePool,
-                    shared: MoeShared, out, stream=None) -> None:
+                    shared: MoeShared, out, stream=None, check: bool = False) -> None:
+    """moe_prefill_forward.  check=True synchronises and raises on a non-zero status."""
     _check(lib.moe_prefill_forward(_ptr(x), t, ctypes.byref(router), ctypes.byref(plan),
                                    ctypes.byref(pool), ctypes.byref(shared), _ptr(out),
                                    _stream(stream)))
+    if check:
+        _status_checked(plan.ws, plan.ws_bytes, stream)
 
 
 def set_stage_events(events) -> None:
