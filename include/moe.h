@@ -168,6 +168,26 @@ int moe_layer_forward(const float *x, int32_t nb, const moe_router *router,
                       moe_slots *slots, const moe_pool *pool,
                       const moe_shared *shared, float *out, void *stream);
 
+/* moe_layer_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, kernels and results as moe_layer_forward,
+ * except that slots->ws must be NULL and slots->ws_bytes 0: the decode
+ * kernel's exchange buffers (counters, act values, slice partials, router
+ * logits) live in the library's static scratch, 3 MiB of device memory per
+ * GPU, held from the first call on that GPU until the process ends (its
+ * first call zero-fills it on `stream` with a kernel).  The call allocates
+ * nothing and calls no allocating routine.  Limit: the decode sections of
+ * moe_workspace_bytes(dims, nb) must fit in 3 MiB (every width up to 512
+ * with hidden up to 4096; width 1024 up to hidden 2048); larger dims return
+ * MOE_EWORKSPACE before any HIP call.  Every call on one GPU shares that
+ * GPU's scratch: calls that overlap in time on one GPU (other streams or
+ * threads) race and give wrong results; serialise them.  The status word of
+ * the scratch is read and cleared with moe_workspace_status(NULL, 0, stream)
+ * on the same device. */
+int moe_layer_forward_noalloc(const float *x, int32_t nb, const moe_router *router,
+                              moe_slots *slots, const moe_pool *pool,
+                              const moe_shared *shared, float *out, void *stream);
+
 /* One prefill chunk of t rows (1..32): route every row, group rows by expert,
  * run each used expert on its rows with MFMA tiles (sub-jobs of at most 16
  * rows), the shared expert on all rows, and combine per row in a fixed order.
@@ -180,7 +200,9 @@ int moe_prefill_forward(const float *x, int32_t t, const moe_router *router,
  * descriptor outside the pool or with tag 3 (that expert was skipped; its
  * contribution is zero); bit 2 set when the decode kernel's bounded wait for
  * another block ran out (its output is then not valid).  Synchronises
- * `stream`, reads the word and clears it; <0 on error. */
+ * `stream`, reads the word and clears it; <0 on error.  ws = NULL with
+ * ws_bytes = 0 reads the static scratch of moe_layer_forward_noalloc on the
+ * current device (MOE_EWORKSPACE if no such call has run there). */
 int moe_workspace_status(void *ws, size_t ws_bytes, void *stream);
 
 /* Profiling hook (the analog of per-phase GPU timestamps): for the calling

@@ -79,13 +79,14 @@ def _load():
     lib.moe_route.argtypes = [vp, ctypes.c_int32, P(MoeRouter), P(MoeShared), P(MoeSlots), vp]
     lib.moe_layer_forward.argtypes = [vp, ctypes.c_int32, P(MoeRouter), P(MoeSlots), P(MoePool),
                                       P(MoeShared), vp, vp]
+    lib.moe_layer_forward_noalloc.argtypes = lib.moe_layer_forward.argtypes
     lib.moe_prefill_forward.argtypes = [vp, ctypes.c_int32, P(MoeRouter), P(MoePrefillPlan),
                                         P(MoePool), P(MoeShared), vp, vp]
     lib.moe_workspace_status.argtypes = [vp, ctypes.c_size_t, vp]
     lib.moe_set_stage_events.argtypes = [P(ctypes.c_void_p), ctypes.c_int32]
     lib.moe_last_error.restype = ctypes.c_char_p
-    for name in ("moe_set_stage_events", "moe_workspace_init", "moe_route", "moe_layer_forward", "moe_prefill_forward",
-                 "moe_workspace_status"):
+    for name in ("moe_set_stage_events", "moe_workspace_init", "moe_route", "moe_layer_forward",
+                 "moe_layer_forward_noalloc", "moe_prefill_forward", "moe_workspace_status"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -164,6 +165,20 @@ def layer_forward(x, nb: int, router: MoeRouter, slots: MoeSlots, pool: MoePool,
         _status_checked(slots.ws, slots.ws_bytes, stream)
 
 
+def layer_forward_noalloc(x, nb: int, router: MoeRouter, slots: MoeSlots, pool: MoePool,
+                          shared: MoeShared, out, stream=None) -> None:
+    """moe_layer_forward_noalloc: slots.ws must be None and slots.ws_bytes 0
+    (the library's static scratch is used)."""
+    _check(lib.moe_layer_forward_noalloc(_ptr(x), nb, ctypes.byref(router), ctypes.byref(slots),
+                                         ctypes.byref(pool), ctypes.byref(shared), _ptr(out),
+                                         _stream(stream)))
+
+
+def static_scratch_status(stream=None) -> int:
+    """Read and clear the status word of the static scratch on the current device."""
+    return _check(lib.moe_workspace_status(None, 0, _stream(stream)))
+
+
 def prefill_forward(x, t: int, router: MoeRouter, plan: MoePrefillPlan, pool: MoePool,
                     shared: MoeShared, out, stream=None, check: bool = False) -> None:
     """moe_prefill_forward.  check=True synchronises and raises on a non-zero status."""
@@ -205,6 +220,12 @@ def make_pool(pool: torch.Tensor) -> MoePool:
 def make_shared(gate: torch.Tensor, rec: int) -> MoeShared:
     assert gate.dtype == torch.bfloat16 and gate.is_contiguous()
     return MoeShared(gate.data_ptr(), int(rec))
+
+
+def slots_without_workspace(slots: MoeSlots) -> MoeSlots:
+    """The same result buffers with no workspace (for moe_layer_forward_noalloc)."""
+    return MoeSlots(slots.tab, slots.wmap, slots.ids, slots.topk_idx, slots.topk_w,
+                    slots.logits, slots.gamma, None, 0)
 
 
 class DecodeBuffers:

@@ -8,8 +8,18 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "moe_internal.h"
+
+// The scratch of moe_layer_forward_noalloc: the decode kernel's exchange
+// buffers (counters, epoch-tagged act values and slice partials, router
+// logits) for callers that cannot allocate.  Each GPU the library runs on
+// holds one copy until the process ends.  Host code never uses this name as
+// an address: the device address of each GPU's copy comes from
+// hipGetSymbolAddress (scratch_on_device below).
+constexpr size_t kStaticScratchBytes = size_t(3) << 20;   // 3 MiB
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 
 namespace moe {
 
@@ -137,7 +147,7 @@ static int stage_done(int i, hipStream_t s) {
   return MOE_OK;
 }
 
-static int check_slots(const moe_slots *s, const moe_dims &d, int nb) {
+static int check_slot_tables(const moe_slots *s) {
   if (!s) return fail(MOE_EINVAL, "slots is NULL");
   REQ(s->tab, 8, "slots.tab");
   REQ(s->wmap, 4, "slots.wmap");
@@ -146,17 +156,44 @@ static int check_slots(const moe_slots *s, const moe_dims &d, int nb) {
   REQ(s->topk_w, 4, "slots.topk_w");
   REQ(s->logits, 8, "slots.logits");
   REQ(s->gamma, 4, "slots.gamma");
+  return MOE_OK;
+}
+
+static int check_slots(const moe_slots *s, const moe_dims &d, int nb) {
+  const int rc = check_slot_tables(s);
+  if (rc) return rc;
   return check_ws(s->ws, s->ws_bytes, d, nb);
 }
 
+// Bytes of the decode sections at the head of the workspace (counters, act,
+// slice partials, router logits): the prefill sections start after them.
+static size_t decode_ws_bytes(const moe_dims &d, int nb) {
+  return workspace_layout(d.hidden, d.inter, d.n_experts, d.top_k, nb).pf_xf;
+}
 
-// The decode launch description shared by moe_route (no pool, no output)
-// and moe_layer_forward; arguments were validated by the caller.
+// Checks shared by moe_layer_forward and moe_layer_forward_noalloc (all but
+// the workspace).
+static int check_forward(const float *x, int nb, const moe_router *router, const moe_slots *slots,
+                         const moe_pool *pool, const moe_shared *shared, const float *out) {
+  int rc = check_router(router);
+  if (rc) return rc;
+  const moe_dims &d = router->dims;
+  if (nb < 1 || nb > MOE_MAX_NB) return fail(MOE_EINVAL, "nb %d: must be in 1..%d", nb, MOE_MAX_NB);
+  REQ(x, 16, "x");
+  REQ(out, 16, "out");
+  if ((rc = check_pool(pool))) return rc;
+  if ((rc = check_shared(shared, d, pool))) return rc;
+  return check_slot_tables(slots);
+}
+
+
+// The decode launch description shared by moe_route (no pool, no output),
+// moe_layer_forward and moe_layer_forward_noalloc (ws = the workspace or the
+// static scratch); arguments were validated by the caller.
 static LayerLaunch layer_launch(const float *x, int nb, const moe_router *router, const moe_slots *slots,
-                                const moe_pool *pool, const moe_shared *shared, float *out) {
+                                const moe_pool *pool, const moe_shared *shared, float *out, uint8_t *ws) {
   const moe_dims &d = router->dims;
   const WorkspaceLayout L = workspace_layout(d.hidden, d.inter, d.n_experts, d.top_k, nb);
-  uint8_t *ws = static_cast<uint8_t *>(slots->ws);
   LayerLaunch l{};
   l.x = x;
   l.nb = nb;
@@ -185,6 +222,41 @@ static LayerLaunch layer_launch(const float *x, int nb, const moe_router *router
   l.slice_gamma = reinterpret_cast<float *>(ws + L.slice_logits +
                                             size_t(kSlices) * kMaxNb * kMaxExperts * sizeof(double));
   return l;
+}
+
+// Device address of this GPU's copy of `scratch`, looked up (and the copy
+// zero-filled on `s`) on the first call on each device.  Under a lock: the
+// lookup and the fill happen once per device.
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static uint8_t *g_scratch_ptr[kMaxDevices] = {};
+
+static int scratch_on_device(hipStream_t s, uint8_t **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ELAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_EINVAL, "device %d: above %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_ELAUNCH, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    // counters start at zero and no act value carries an epoch tag yet
+    e = launch_fill_zero(p, kStaticScratchBytes, s);
+    if (e != hipSuccess) return fail(MOE_ELAUNCH, "scratch fill on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<uint8_t *>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+// The copy of `scratch` on the current device, if a call has set it up.
+static uint8_t *scratch_if_set_up() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace moe
@@ -223,25 +295,41 @@ int moe_route(const float *x, int32_t nb, const moe_router *router, const moe_sh
   REQ(x, 16, "x");
   if ((rc = check_shared(shared, d, nullptr))) return rc;
   if ((rc = check_slots(slots, d, nb))) return rc;
-  const LayerLaunch l = layer_launch(x, nb, router, slots, nullptr, shared, nullptr);
+  const LayerLaunch l =
+      layer_launch(x, nb, router, slots, nullptr, shared, nullptr, static_cast<uint8_t *>(slots->ws));
   rc = launched(launch_route_only(l, static_cast<hipStream_t>(stream)), "route");
   return rc ? rc : ok();
 }
 
 int moe_layer_forward(const float *x, int32_t nb, const moe_router *router, moe_slots *slots,
                       const moe_pool *pool, const moe_shared *shared, float *out, void *stream) {
-  int rc = check_router(router);
+  int rc = check_forward(x, nb, router, slots, pool, shared, out);
   if (rc) return rc;
-  const moe_dims &d = router->dims;
-  if (nb < 1 || nb > MOE_MAX_NB) return fail(MOE_EINVAL, "nb %d: must be in 1..%d", nb, MOE_MAX_NB);
-  REQ(x, 16, "x");
-  REQ(out, 16, "out");
-  if ((rc = check_pool(pool))) return rc;
-  if ((rc = check_shared(shared, d, pool))) return rc;
-  if ((rc = check_slots(slots, d, nb))) return rc;
+  if ((rc = check_ws(slots->ws, slots->ws_bytes, router->dims, nb))) return rc;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const LayerLaunch l = layer_launch(x, nb, router, slots, pool, shared, out);
+  const LayerLaunch l = layer_launch(x, nb, router, slots, pool, shared, out, static_cast<uint8_t *>(slots->ws));
+  if ((rc = launched(launch_layer(l, s), "layer"))) return rc;
+  if ((rc = stage_done(0, s))) return rc;
+  return ok();
+}
+
+int moe_layer_forward_noalloc(const float *x, int32_t nb, const moe_router *router, moe_slots *slots,
+                              const moe_pool *pool, const moe_shared *shared, float *out, void *stream) {
+  int rc = check_forward(x, nb, router, slots, pool, shared, out);
+  if (rc) return rc;
+  if (slots->ws || slots->ws_bytes)
+    return fail(MOE_EINVAL, "slots.ws must be NULL and slots.ws_bytes 0: moe_layer_forward_noalloc "
+                "uses the library's static scratch");
+  const size_t need = decode_ws_bytes(router->dims, nb);
+  if (need > kStaticScratchBytes)
+    return fail(MOE_EWORKSPACE, "these dims need %zu bytes of decode scratch, above the %zu-byte static "
+                "scratch of moe_layer_forward_noalloc (use moe_layer_forward with a workspace)",
+                need, kStaticScratchBytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t *ws = nullptr;
+  if ((rc = scratch_on_device(s, &ws))) return rc;
+  const LayerLaunch l = layer_launch(x, nb, router, slots, pool, shared, out, ws);
   if ((rc = launched(launch_layer(l, s), "layer"))) return rc;
   if ((rc = stage_done(0, s))) return rc;
   return ok();
@@ -305,6 +393,11 @@ int moe_prefill_forward(const float *x, int32_t t, const moe_router *router, moe
 }
 
 int moe_workspace_status(void *ws, size_t ws_bytes, void *stream) {
+  if (!ws && ws_bytes == 0) {   // the static scratch of moe_layer_forward_noalloc on this device
+    ws = scratch_if_set_up();
+    if (!ws) return fail(MOE_EWORKSPACE, "no moe_layer_forward_noalloc call has run on this device");
+    ws_bytes = kStaticScratchBytes;
+  }
   if (!ws || ws_bytes < kSyncWords * sizeof(uint32_t)) return fail(MOE_EWORKSPACE, "workspace is NULL or too small");
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint32_t *word = static_cast<uint32_t *>(ws) + kSyncStatus;

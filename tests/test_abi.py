@@ -130,3 +130,26 @@ def test_route_and_init_validation():
     assert rc == moe.EINVAL
     assert moe.lib.moe_workspace_init(None, 256, None) == moe.EWORKSPACE
     assert moe.lib.moe_workspace_init(A + 3, 256, None) == moe.EINVAL
+
+
+def _noalloc(nb=1, **kw):
+    d, router, pool, shared, slots = _args(**kw)
+    s0 = moe.slots_without_workspace(slots)
+    return moe.lib.moe_layer_forward_noalloc(A * 4, nb, ctypes.byref(router), ctypes.byref(s0),
+                                             ctypes.byref(pool), ctypes.byref(shared), A * 5, None), slots
+
+
+def test_noalloc_rejects_before_any_hip_call():
+    # sizes past the 3 MiB static scratch, a caller workspace, and the usual checks
+    rc, _ = _noalloc(I=2048)
+    assert rc == moe.EWORKSPACE and "static" in moe.last_error()
+    rc, _ = _noalloc(H=4096, I=1024)
+    assert rc == moe.EWORKSPACE
+    d, router, pool, shared, slots = _args()
+    rc = moe.lib.moe_layer_forward_noalloc(A * 4, 1, ctypes.byref(router), ctypes.byref(slots),
+                                           ctypes.byref(pool), ctypes.byref(shared), A * 5, None)
+    assert rc == moe.EINVAL and "ws must be NULL" in moe.last_error()
+    rc, _ = _noalloc(nb=5)
+    assert rc == moe.EINVAL and "nb" in moe.last_error()
+    rc, _ = _noalloc(H=300)
+    assert rc == moe.EINVAL and "hidden" in moe.last_error()
