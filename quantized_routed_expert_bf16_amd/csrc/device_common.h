@@ -285,6 +285,11 @@ __device__ inline uint64_t order_key(double v) {
   const uint64_t b = __double_as_longlong(v);
   return (b >> 63) ? ~b : (b | (uint64_t(1) << 63));
 }
+// Order-preserving u32 key of a float (larger float <-> larger key).
+__device__ inline uint32_t order_key32(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b >> 31) ? ~b : (b | 0x80000000u);
+}
 template <int CTRL>
 __device__ inline uint64_t dpp_u64(uint64_t v) {
   const int lo = __builtin_amdgcn_mov_dpp(int(uint32_t(v)), CTRL, 0xF, 0xF, true);

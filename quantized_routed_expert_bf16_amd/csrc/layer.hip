@@ -69,6 +69,7 @@ struct LayerArgs {
   int tiles;         // down tiles (of kRowsPerTile rows)
   int per_slice;     // blocks per slice (gridDim.x / 8)
   int route_blocks;  // router blocks in all (block g = lr * n_slices + x)
+  uint32_t d_codes[3], d_sb[3];   // down section offsets in a record, per bits tag 0..2
 };
 
 __device__ inline uint32_t *sw(const LayerArgs &a, int x, int field) {
@@ -105,6 +106,7 @@ struct Shared {
   double selv[NB][kMaxTopK];
   float wsel[NB][kMaxTopK];
   int uid[kSlotStride];
+  int first[NB > 1 ? kMaxExperts : 1];   // union: lowest (row, rank) entry per expert
   float wslot[NB][kSlotStride];   // routing weight per slot (index u: gamma)
   uint64_t desc[kSlotStride];     // descriptor per slot (index u: shared expert)
   const uint8_t *dcodes[kSlotStride];   // down codes of the slot's record (null: skip)
@@ -190,16 +192,52 @@ __device__ __forceinline__ void router_rows(const LayerArgs &a, const float *xs,
   }
 }
 
+// Of the keys kk (0: not a candidate), the `need` largest in the order (key
+// descending, lower index first): a most-significant-bit-first radix select
+// with ballot counts finds the longest prefix T that at least `need` keys
+// reach (stopping as soon as exactly `need` do); keys above T are taken and,
+// of the keys equal to T, the lowest indices fill the remaining places.
+template <typename K, int kJ>
+__device__ __forceinline__ void radix_take(const K (&kk)[kJ], int need, bool (&take)[kJ]) {
+  const int lane = threadIdx.x & 63;
+  constexpr int kBits = 8 * sizeof(K);
+  K T = 0;
+  int cnt = kJ * 64;   // keys >= T (before the first step: every key)
+  for (int bit = kBits - 1; bit >= 0 && cnt != need; --bit) {
+    const K c = T | (K(1) << bit);
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) n += __popcll(__ballot(kk[j] >= c));
+    if (n >= need) {
+      T = c;
+      cnt = n;
+    }
+  }
+  int left = need;   // places left for keys equal to T
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) left -= __popcll(__ballot(kk[j] > T));
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  int eq_before = 0;
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const bool eq = kk[j] == T && T != 0;
+    const uint64_t eqm = __ballot(eq);
+    take[j] = kk[j] > T || (eq && eq_before + __popcll(eqm & below) < left);
+    eq_before += __popcll(eqm);
+  }
+}
+
 // Top-k of the published logits (every block).  Wave b (b < NB) holds row
-// b's logits in registers, expert lane + 64 j in register j, with 64-bit
-// order-preserving keys of the float64 values.  A most-significant-bit-first
-// radix select (ballot counts) finds the longest key prefix T that at least
-// k keys reach; it stops early once exactly k do.  Keys above T are selected
-// and, of the keys equal to T (equal logits), the lowest ids fill the
-// remaining places, which is the order (logit descending, id ascending).
-// The k selected entries are ranked against each other in registers (the
-// wave walks the selected lanes with readlane): s.sel[b][rank] and
-// s.selv[b][rank] on return.
+// b's logits in registers, expert lane + 64 j in register j.  The select runs
+// on 32-bit order-preserving keys of the logits rounded to float32 (rounding
+// never reverses an order, so a key above the float32 threshold T is in the
+// top k and a key below it is not); only logits whose float32 rounding equals
+// T are ranked again on their 64-bit keys of the float64 values, with ties
+// to the lower expert id, which is the order (logit descending, id
+// ascending).  In the common case T's group is exactly the places left and
+// no 64-bit step runs.  The k selected entries are then ranked against each
+// other in registers (the wave walks the selected lanes with readlane):
+// s.sel[b][rank] and s.selv[b][rank] on return.
 // kJ = 2 serves up to 128 experts, 4 up to 256.
 template <int NB, int kJ>
 __device__ __forceinline__ void select_row(const LayerArgs &a, Shared<NB> &s, const double *lg, const float *gm,
@@ -212,41 +250,64 @@ __device__ __forceinline__ void select_row(const LayerArgs &a, Shared<NB> &s, co
     v[j] = ld_dev(lg + b * kMaxExperts + min(lane + 64 * j, E - 1));
   const float gam = ld_dev(gm + b);
   uint64_t kk[kJ];
+  uint32_t k32[kJ];
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
     // + 0.0 folds -0 into +0 so that equal logits tie on the id alone;
-    // padding keys are 0, below every finite logit's key and below every
-    // prefix the select tries
+    // padding keys are 0, below every logit's key and below every prefix
+    // the select tries
     const bool in = lane + 64 * j < E;
-    kk[j] = in ? order_key(v[j] + 0.0) : 0;
+    const double vv = v[j] + 0.0;
+    kk[j] = in ? order_key(vv) : 0;
+    k32[j] = in ? order_key32(float(vv)) : 0;
   }
-  uint64_t T = 0;
-  int cnt = kJ * 64;   // keys >= T
-  for (int bit = 63; bit >= 0 && cnt != k; --bit) {
-    const uint64_t c = T | (uint64_t(1) << bit);
-    int n = 0;
+  // float32 keys: T = the k-th largest key, gt keys above it, neq equal to it
+  // two key bits per step: the three candidate prefixes are counted
+  // independently, and the largest one that k keys reach is kept
+  uint32_t T = 0;
+  int cnt = kJ * 64;
+  for (int bit = 30; bit >= 0 && cnt != k; bit -= 2) {
+    const uint32_t c1 = T | (1u << bit), c2 = T | (2u << bit), c3 = T | (3u << bit);
+    int n1 = 0, n2 = 0, n3 = 0;
 #pragma unroll
-    for (int j = 0; j < kJ; ++j) n += __popcll(__ballot(kk[j] >= c));
-    if (n >= k) {
-      T = c;
-      cnt = n;
+    for (int j = 0; j < kJ; ++j) {
+      n1 += __popcll(__ballot(k32[j] >= c1));
+      n2 += __popcll(__ballot(k32[j] >= c2));
+      n3 += __popcll(__ballot(k32[j] >= c3));
+    }
+    if (n3 >= k) {
+      T = c3;
+      cnt = n3;
+    } else if (n2 >= k) {
+      T = c2;
+      cnt = n2;
+    } else if (n1 >= k) {
+      T = c1;
+      cnt = n1;
     }
   }
-  int need = k;   // places left for keys equal to T
-#pragma unroll
-  for (int j = 0; j < kJ; ++j) need -= __popcll(__ballot(kk[j] > T));
-  const uint64_t below = (uint64_t(1) << lane) - 1;
-  int eq_before = 0;
-  bool take[kJ];
-  uint64_t tm[kJ];
+  int gt = 0, neq = 0;
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
-    const bool eq = kk[j] == T;
-    const uint64_t eqm = __ballot(eq);
-    take[j] = kk[j] > T || (eq && eq_before + __popcll(eqm & below) < need);
-    tm[j] = __ballot(take[j]);
-    eq_before += __popcll(eqm);
+    gt += __popcll(__ballot(k32[j] > T));
+    neq += __popcll(__ballot(k32[j] == T));
   }
+  bool take[kJ];
+  if (neq == k - gt) {   // T's group fills the places left exactly
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) take[j] = k32[j] >= T;
+  } else {               // equal in float32: the float64 values and ids decide
+    uint64_t km[kJ];
+    bool te[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) km[j] = k32[j] == T ? kk[j] : 0;
+    radix_take<uint64_t, kJ>(km, k - gt, te);
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) take[j] = k32[j] > T || te[j];
+  }
+  uint64_t tm[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) tm[j] = __ballot(take[j]);
   // rank the k selected entries against each other in registers: the
   // wave walks the selected lanes (uniform masks) and reads each entry's
   // key with readlane
@@ -306,13 +367,13 @@ __device__ __forceinline__ void route_union(const LayerArgs &a, Shared<NB> &s, c
     // float64 softmax)
     const float ex = ent ? expf(float(s.selv[lb][lr] - s.selv[lb][0])) : 0.0f;
     s.exq[lane] = ex;
-    // first-seen union: fq = lowest entry with this lane's expert
+    // first-seen union: fq = lowest entry with this lane's expert (an LDS
+    // minimum per expert id; one wave, whose LDS operations run in order)
     int fq = lane;
     if constexpr (NB > 1) {
-      for (int q = 0; q < n; ++q) {
-        const int eq = __builtin_amdgcn_readlane(e_l, q);
-        fq = (eq == e_l && q < fq) ? q : fq;
-      }
+      if (ent) s.first[e_l] = 64;
+      if (ent) atomicMin(&s.first[e_l], lane);
+      if (ent) fq = s.first[e_l];
     }
     const bool first = ent && fq == lane;
     const uint64_t mask = __ballot(first);
@@ -879,47 +940,89 @@ __device__ __forceinline__ void combine_tile(const LayerArgs &a, const Shared<NB
 // of the slice, and slots g, g + SG, ...; weights for the lane's slots are
 // loaded before the wait for the slice's gate/up units, the act chunks with
 // device-coherent loads after it.
+// The lane's down weights of one batch of slots (the batch starting at slot
+// s0): code words and (scale, bias) words.  Addresses come from the pool
+// argument and the host-computed section offsets (global loads, which LDS
+// waits never wait for).
+// Slots per lane per down batch: with one row the union has at most k + 1
+// <= 16 slots, which four per lane cover at 64 columns per slice (and a
+// shorter unrolled batch keeps the kernel's code small).
 template <int NB>
-__device__ __forceinline__ void run_down(const LayerArgs &a, Shared<NB> &sh, int x, int tile, float *act_lds,
-                         float *asum_lds) {
+constexpr int slot_batch() { return NB == 1 ? 4 : kSlotBatch; }
+
+template <int NB>
+struct DownRegs {
+  uint32_t w[slot_batch<NB>()][4];
+  uint32_t sbw[slot_batch<NB>()];
+};
+
+template <int NB>
+__device__ __forceinline__ void down_load(const LayerArgs &a, const Shared<NB> &sh, int x, int tile, int s0,
+                                          DownRegs<NB> &r) {
+  constexpr int kSB = slot_batch<NB>();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int H = a.l.hidden, I = a.l.inter, W = a.W;
-  const int cpr = W / kChunk;                 // chunks per row in the slice (1..8)
-  const int sg = 8 / cpr;                     // slot groups per row
+  const int H = a.l.hidden, W = a.W;
+  const int cpr = W / kChunk, sg = 8 / cpr;
   const int idx = lane & 7;
   const int rw = lane >> 3, c = idx % cpr, g = idx / cpr;
   const int row = tile * kRowsPerTile + wave * kRowsPerWave + rw;
-  const int col = x * W + c * kChunk;        // first column of this lane's chunk
+  const int col = x * W + c * kChunk;
   const int grp = col / kGroup, half = (col % kGroup) / kChunk;
+  const int n_slots = sh.u + 1;
+  // section offsets read with constant indices (scalar loads of the kernel
+  // arguments), then chosen per lane by the bits tag
+  const uint32_t dc0 = a.d_codes[0], dc1 = a.d_codes[1], dc2 = a.d_codes[2];
+  const uint32_t ds0 = a.d_sb[0], ds1 = a.d_sb[1], ds2 = a.d_sb[2];
+#pragma unroll
+  for (int m = 0; m < kSB; ++m) {
+    const int slot = s0 + g + sg * m;
+    r.w[m][0] = r.w[m][1] = r.w[m][2] = r.w[m][3] = 0;
+    r.sbw[m] = 0;
+    const int bt = slot < n_slots ? sh.dbits[slot] : 0;
+    if (bt) {
+      const uint64_t d = sh.desc[slot];
+      const uint8_t *rec = a.l.pool + (d & ~uint64_t(255));
+      const uint32_t dco = bt == 4 ? dc0 : (bt == 3 ? dc1 : dc2);
+      const uint32_t dso = bt == 4 ? ds0 : (bt == 3 ? ds1 : ds2);
+      const uint8_t *grow = rec + dco + (size_t(grp) * H + row) * (kGroup * bt / 8);
+      if (__builtin_expect(bt == 4, 1)) load_chunk<4>(grow, kGroup, half, r.w[m]);
+      else if (bt == 3) load_chunk<3>(grow, kGroup, half, r.w[m]);
+      else load_chunk<2>(grow, kGroup, half, r.w[m]);
+      r.sbw[m] = reinterpret_cast<const uint32_t *>(rec + dso)[size_t(grp) * H + row];
+    }
+  }
+}
+
+template <int NB>
+__device__ __forceinline__ void publish_partial(const LayerArgs &a, Shared<NB> &sh, int x, int tile, float (&acc)[NB]);
+
+template <int NB>
+__device__ __forceinline__ void run_down(const LayerArgs &a, Shared<NB> &sh, int x, int tile, float *act_lds,
+                         float *asum_lds) {
+  const int lane = threadIdx.x & 63;
+  const int I = a.l.inter, W = a.W;
+  const int cpr = W / kChunk;                 // chunks per row in the slice (1..8)
+  const int sg = 8 / cpr;                     // slot groups per row
+  const int idx = lane & 7;
+  const int c = idx % cpr, g = idx / cpr;
   const int u = sh.u, n_slots = u + 1;
+  constexpr int kSB = slot_batch<NB>();
   float acc[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = 0.0f;
 
-  for (int s0 = 0; s0 < n_slots; s0 += sg * kSlotBatch) {
+  for (int s0 = 0; s0 < n_slots; s0 += sg * kSB) {
     // 1. this lane's weights for the batch
-    uint32_t w[kSlotBatch][4];
-    uint32_t sbw[kSlotBatch];
-#pragma unroll
-    for (int m = 0; m < kSlotBatch; ++m) {
-      const int slot = s0 + g + sg * m;
-      w[m][0] = w[m][1] = w[m][2] = w[m][3] = 0;
-      sbw[m] = 0;
-      const int bt = slot < n_slots ? sh.dbits[slot] : 0;
-      if (bt) {
-        const uint8_t *grow = sh.dcodes[slot] + (size_t(grp) * H + row) * (kGroup * bt / 8);
-        if (bt == 4) load_chunk<4>(grow, kGroup, half, w[m]);
-        else if (bt == 3) load_chunk<3>(grow, kGroup, half, w[m]);
-        else load_chunk<2>(grow, kGroup, half, w[m]);
-        sbw[m] = sh.dsb[slot][size_t(grp) * H + row];
-      }
-    }
+    DownRegs<NB> r;
+    down_load<NB>(a, sh, x, tile, s0, r);
+    uint32_t (&w)[kSB][4] = r.w;
+    uint32_t (&sbw)[kSB] = r.sbw;
     // 2. the slice's act values must be complete
     if (s0 == 0) wait_geq(a, sw(a, x, kSliceGu), uint32_t(n_slots * a.ups));
     // 3. stage the batch's act chunks in LDS: one device-coherent 16-byte
     //    load per thread; 8 consecutive threads hold one 32-value chunk and
     //    form its sum with a DPP group-of-8 reduction
-    const int nb_slots = min(n_slots - s0, sg * kSlotBatch);
+    const int nb_slots = min(n_slots - s0, sg * kSB);
     const int n_f4 = nb_slots * NB * (W / 4);
     __syncthreads();
     constexpr int kStIt = 4;   // loads in flight per thread
@@ -978,7 +1081,7 @@ __device__ __forceinline__ void run_down(const LayerArgs &a, Shared<NB> &sh, int
     __syncthreads();
     // 4. accumulate the lane's slots
 #pragma unroll
-    for (int m = 0; m < kSlotBatch; ++m) {
+    for (int m = 0; m < kSB; ++m) {
       const int sl = g + sg * m;
       const int slot = s0 + sl;
       const int bt = slot < n_slots ? sh.dbits[slot] : 0;
@@ -986,7 +1089,7 @@ __device__ __forceinline__ void run_down(const LayerArgs &a, Shared<NB> &sh, int
       float P[NB];
       // runs of W + 4 floats: the slot groups of a row read different banks
       const LdsX ax{act_lds + sl * NB * (W + kStagePad) + c * kChunk, W + kStagePad};
-      if (bt == 4) chunk_dot<4, NB>(w[m], ax, P);
+      if (__builtin_expect(bt == 4, 1)) chunk_dot<4, NB>(w[m], ax, P);
       else if (bt == 3) chunk_dot<3, NB>(w[m], ax, P);
       else chunk_dot<2, NB>(w[m], ax, P);
       const float sc = sb_scale(sbw[m]), bi = sb_bias(sbw[m]);
@@ -995,11 +1098,19 @@ __device__ __forceinline__ void run_down(const LayerArgs &a, Shared<NB> &sh, int
         acc[b] = fmaf(sh.wslot[b][slot], fmaf(sc, P[b], bi * asum_lds[(sl * NB + b) * cpr + c]), acc[b]);
     }
   }
-  // sum the row's 8 lanes (chunks x slot groups) and publish the slice
-  // partial, tagged with this call's epoch: no wait and no counter, the
-  // combining block checks every partial's tag
+  publish_partial<NB>(a, sh, x, tile, acc);
+}
+
+// Sum the row's 8 lanes (chunks x slot groups) and publish the slice
+// partial, tagged with this call's epoch: no wait and no counter, the
+// combining block checks every partial's tag.  Then the tile's combine.
+template <int NB>
+__device__ __forceinline__ void publish_partial(const LayerArgs &a, Shared<NB> &sh, int x, int tile, float (&acc)[NB]) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = group8_sum(acc[b]);
+  const int H = a.l.hidden;
+  const int row = tile * kRowsPerTile + (threadIdx.x >> 6) * kRowsPerWave + (lane >> 3);
   if ((threadIdx.x & 7) == 0)
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -1348,24 +1459,20 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
         gate_up_load_any<CPL>(a, d0, gate_up_row0(a, x, i - slot0 * a.ups), pre);
       asm volatile("" ::: "memory");   // the loads are issued here, not sunk to their use
       route_union<NB>(a, sh, rec_lds);
+      const int n_gu = sh.u * a.ups;
       if (early) {   // slot0 < k <= u: a gate/up unit
         run_gate_up<NB, CPL, true>(a, x, d0, slot0, i - slot0 * a.ups, xs, xsum, sh.ep, pre);
         i += P;
       }
-    }
-    const int u = sh.u;
-    const int n_gu = u * a.ups;
-    const int n_total = n_gu + a.tiles;
-    if constexpr (!kM) {
       for (; i < n_gu; i += P) {
         const int slot = i / a.ups;
         gate_up_item<NB, CPL, kM>(a, x, sh.desc[slot], slot, i - slot * a.ups, xs, xsum, xb, xg, red, sh.ep);
       }
+      for (; i < n_gu + a.tiles; i += P) run_down<NB>(a, sh, x, i - n_gu, act_lds, asum_lds);
     }
     if constexpr (kM) {
-      for (; i < n_total; i += P) run_down_m<NB>(a, sh, x, i - n_gu, xb, xg, red);
-    } else {
-      for (; i < n_total; i += P) run_down<NB>(a, sh, x, i - n_gu, act_lds, asum_lds);
+      const int n_gu = sh.u * a.ups;
+      for (; i < n_gu + a.tiles; i += P) run_down_m<NB>(a, sh, x, i - n_gu, xb, xg, red);
     }
   } else if (threadIdx.x == 0) {
     // a block of a slice without columns (I < 8 * 32) still reads the call's
@@ -1500,6 +1607,11 @@ hipError_t launch_layer(const LayerLaunch &l, hipStream_t s) {
   a.ups = a.W / kTileRowPairs;
   a.tiles = l.hidden / kRowsPerTile;
   if (a.tiles > kMaxDownTiles || a.W / kChunk > 8 || a.W % kTileRowPairs) return hipErrorInvalidValue;
+  for (int tag = 0; tag < 3; ++tag) {
+    const RecordLayout L = record_layout(l.hidden, l.inter, 4 - tag);
+    a.d_codes[tag] = uint32_t(L.d_codes);
+    a.d_sb[tag] = uint32_t(L.d_sb);
+  }
   const bool two = l.hidden > 64 * kChunk;
   // two to four rows at H = 2048 and 64 columns per slice: gate/up units and
   // down tiles on MFMA

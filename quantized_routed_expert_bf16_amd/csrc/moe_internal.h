@@ -102,7 +102,6 @@ constexpr int kSyncStatus = 520;            // bit 0: bad descriptor skipped; bi
 constexpr int kSyncExit = 528;              // slices whose blocks all left
 constexpr int kSyncAbort = 576;             // set when a wait ran out: all waits fall through
 constexpr int kSyncEpoch = 608;             // decode: number of the last finished call (tags data)
-constexpr int kSyncTile = 640;              // 256 words: slices done per down row tile
 constexpr int kMaxDownTiles = 256;
 
 // ------------------------------------------------------------- launchers
