@@ -8,4 +8,5 @@ from .moe_oracle import (  # noqa: F401
     record_layout, unpack_codes, bf16_to_f64, dequant, read_expert,
     router_logits, topk_softmax, route, union_slots, silu, sigmoid,
     expert_mlp, shared_gate, layer_forward, expert_csr, prefill_forward,
+    requantize_group_codes, repack_record,
 )

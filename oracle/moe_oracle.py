@@ -284,3 +284,80 @@ def prefill_forward(x, router_bf16, rec, pool, gvec_bf16, shared_desc, k,
         acc[r_] += gamma[r_] * y
     return {"out": acc.astype(np.float32), "out_f64": acc, "logits": logits,
             "topk_idx": idx, "topk_w": w, "gamma": gamma, **csr}
+
+
+# ------------------------------------------------------------- low-bit store --
+# The pages build a 3- or 2-bit copy of every expert record from the 4-bit
+# source once (gpu/load.rs source page, load_bounded: the low-bit store set
+# up by lowbit::ensure_with_policy, a record stride below the 4-bit one) and
+# give no rule for the requantization.  The reading taken here is plain
+# min/max affine requantization of each 64-code group of dequantised
+# weights, w = q s + b: the group's weights span [lo, hi] with lo and hi at
+# its extreme codes, and the new grid of 2^bits - 1 steps spans the same
+# interval.  Because w is affine in q, the new code of every weight is an
+# exact rational of the old codes, rounded half up, so it is computed in
+# integers; the new scale and bias are float32 operations rounded to bf16.
+
+def _f32_to_bf16_rne(v: np.ndarray) -> np.ndarray:
+    """float32 values -> bf16 bit patterns, round to nearest even (finite v)."""
+    u = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return (rounded & 0xFFFF).astype(np.uint16)
+
+
+def requantize_group_codes(q: np.ndarray, s16: np.ndarray, b16: np.ndarray, bits: int):
+    """Requantize groups of 64 4-bit codes (q [n][64], with bf16 scale and
+    bias bit patterns [n]) to `bits` bits.  Returns (codes [n][64], scale
+    bf16 [n], bias bf16 [n])."""
+    q = np.asarray(q, dtype=np.int64)
+    s = bf16_to_f64(s16).astype(np.float32)
+    b = bf16_to_f64(b16).astype(np.float32)
+    levels = (1 << bits) - 1
+    qmin, qmax = q.min(axis=1), q.max(axis=1)
+    neg = s < 0
+    q_lo = np.where(neg, qmax, qmin)          # code of the smallest weight
+    q_hi = np.where(neg, qmin, qmax)          # code of the largest weight
+    d = np.abs(q_hi - q_lo)                    # steps between them, 0..15
+    t = np.abs(q - q_lo[:, None]) * levels     # (w - lo) / s_old in new-step units times d
+    safe_d = np.maximum(d, 1)[:, None]
+    codes = np.where(d[:, None] > 0, (2 * t + safe_d) // (2 * safe_d), 0)
+    # scale: |s| d / levels (|s| d is exact in float32), bias: b + s q_lo
+    step = (np.abs(s) * d.astype(np.float32)) / np.float32(levels)
+    bias = b + s * q_lo.astype(np.float32)
+    step = np.where(d > 0, step, np.float32(0.0)).astype(np.float32)
+    return codes, _f32_to_bf16_rne(step), _f32_to_bf16_rne(bias.astype(np.float32))
+
+
+def repack_record(pool, desc: int, bits: int, hidden: int, inter: int) -> dict:
+    """A 4-bit record requantized to `bits` bits: raw codes and bf16 (s, b)
+    in the layout the record writer takes (gate/up [2I][H], [2I][H/64];
+    down [H][I], [H][I/64])."""
+    desc = int(desc)
+    assert BITS_OF_TAG[desc & 0x3] == 4, "the source record must be 4-bit"
+    base = desc & ~0xFF
+    lay = record_layout(hidden, inter, 4)
+
+    def sect(name):
+        o, size = lay[name]
+        return np.asarray(pool[base + o: base + o + size], dtype=np.uint8)
+
+    gu_q = unpack_codes(sect("gu_codes").reshape(2 * inter, -1), hidden, 4)
+    gu_sb = sect("gu_sb").view("<u4").reshape(2 * inter, hidden // GROUP)
+    n_groups = inter // GROUP
+    d_grouped = unpack_codes(sect("d_codes").reshape(n_groups * hidden, -1), GROUP, 4)
+    d_sb = sect("d_sb").view("<u4").reshape(n_groups, hidden)     # [group][row]
+
+    def requant(codes_rows, sb_words):
+        rows, n = codes_rows.shape
+        g = codes_rows.reshape(rows * (n // GROUP), GROUP)
+        w = sb_words.reshape(-1)
+        c, s16, b16 = requantize_group_codes(g, w & 0xFFFF, w >> 16, bits)
+        return c.reshape(rows, n), s16.reshape(sb_words.shape), b16.reshape(sb_words.shape)
+
+    gq, gs, gb = requant(gu_q, gu_sb)
+    # down groups are stored group-major: row r of group g holds codes 64g..64g+63 of row r
+    dq_g, ds_g, db_g = requant(d_grouped, d_sb.reshape(-1, 1))
+    dq = dq_g.reshape(n_groups, hidden, GROUP).transpose(1, 0, 2).reshape(hidden, inter)
+    ds = ds_g.reshape(n_groups, hidden).T
+    db = db_g.reshape(n_groups, hidden).T
+    return {"gu_q": gq, "gu_s": gs, "gu_b": gb, "d_q": dq, "d_s": ds, "d_b": db}
