@@ -129,7 +129,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="decode_nb1")
-    ap.add_argument("--extra", default="verify_nb4,lowbit_q3,lowbit_q2,mixed_q4q2,prefill_t32",
+    ap.add_argument("--extra", default="verify_nb4,lowbit_q3,lowbit_q2,mixed_q4q2,prefill_t32,repack",
                     help="comma-separated further configurations reported under 'extra'")
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
     ap.add_argument("--chunk", type=int, default=25, help="steps per captured graph")
@@ -536,6 +536,45 @@ def bench_prefill(moe, torch, syn, name, args):
     return out
 
 
+def bench_repack(moe, torch, syn, args):
+    """The low-bit store builder on one full-shape layer: the 128 4-bit
+    records requantized to 3 and to 2 bits in one call each, timed with HIP
+    events around repeated calls on the launch stream."""
+    cfg = syn.CONFIGS["decode_nb1"]
+    H, I, E = cfg.hidden, cfg.inter, cfg.n_experts
+    p = syn.make_problem(cfg, seed=args.seed, device="cuda", n_layers=1)
+    src = p.rec[0].contiguous()
+    out = {"config": "repack", "records": E,
+           "description": "one layer of 128 hidden-2048 width-512 4-bit records requantized"}
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for bits in (3, 2):
+        rb = moe.record_bytes(H, I, bits)
+        dst = torch.tensor([e * rb | {3: 1, 2: 2}[bits] for e in range(E)], dtype=torch.int64, device="cuda")
+        store = torch.zeros(E * rb, dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            moe.repack(p.pool, src, store, dst, E, H, I, status=status)
+        torch.cuda.synchronize()
+        reps = 20
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            moe.repack(p.pool, src, store, dst, E, H, I, status=status)
+        b.record()
+        torch.cuda.synchronize()
+        if int(status.item()):
+            raise SystemExit(f"repack to {bits} bits: status {int(status.item())}")
+        us = a.elapsed_time(b) * 1e3 / reps
+        moved = E * (moe.record_bytes(H, I, 4) + rb)
+        out[f"q{bits}"] = {"us_per_layer": us, "bytes_per_layer": moved,
+                           "gbs": moved / (us * 1e-6) / 1e9,
+                           "hbm_frac": moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        log(f"repack to {bits} bits: {us:.1f} us per layer of {E} records, "
+            f"{moved / (us * 1e-6) / 1e9:.0f} GB/s")
+    del p
+    torch.cuda.empty_cache()
+    return out
+
+
 def pct(v, q):
     v = sorted(v)
     return v[min(len(v) - 1, int(q * (len(v) - 1) + 0.5))]
@@ -733,7 +772,9 @@ def main():
     main_res = bench_decode(moe, torch, syn, args.config, args, with_cpu=not args.no_cpu)
     extra = {}
     for name in [n for n in args.extra.split(",") if n]:
-        if syn.CONFIGS[name].prefill:
+        if name == "repack":
+            extra[name] = bench_repack(moe, torch, syn, args)
+        elif syn.CONFIGS[name].prefill:
             extra[name] = bench_prefill(moe, torch, syn, name, args)
         else:
             extra[name] = bench_decode(moe, torch, syn, name, args, with_cpu=False)

@@ -196,6 +196,32 @@ int moe_prefill_forward(const float *x, int32_t t, const moe_router *router,
                         moe_prefill_plan *plan, const moe_pool *pool,
                         const moe_shared *shared, float *out, void *stream);
 
+/* Low-bit store builder: the engine keeps a 3- or 2-bit copy of every
+ * expert record, built once from the 4-bit source (gpu/load.rs source page,
+ * load_bounded: the low-bit store and its smaller record stride; the pages
+ * give no requantization rule).  For i < n_records, the 4-bit record at
+ * src_desc[i] (tag 0) in the source pool is requantized into a record of
+ * dst_desc[i]'s width (tag 1 = 3-bit, 2 = 2-bit) at its offset in the
+ * destination pool.  Rule (min/max affine requantization of each 64-code
+ * group of dequantised weights w = q s + b, exact in the code domain): with
+ * q_lo and q_hi the group's codes of its smallest and largest weight and
+ * d = |q_hi - q_lo|, the new code of a weight is round_half_up(|q - q_lo|
+ * (2^bits - 1) / d), the new scale bf16(|s| d / (2^bits - 1)) and the new bias
+ * bf16(b + s q_lo) (float32 operations, bf16 round to nearest even; codes 0
+ * and scale 0 when d = 0).
+ *   src_pool/dst_pool: device, 256-byte aligned, src_bytes/dst_bytes long
+ *     (may be the same pool when the records do not overlap).
+ *   src_desc/dst_desc: device arrays [n_records] of record descriptors.
+ *   status: device u32 or NULL; bit 0 is OR-ed in when a descriptor pair is
+ *     invalid (wrong tag, or a record outside its pool): that record is
+ *     skipped, the others are written.
+ * Validation of the shape and pointers happens on the host before any HIP
+ * call; one kernel launch on `stream`. */
+int moe_repack(const uint8_t *src_pool, uint64_t src_bytes, const uint64_t *src_desc,
+               uint8_t *dst_pool, uint64_t dst_bytes, const uint64_t *dst_desc,
+               int32_t n_records, int32_t hidden, int32_t inter, uint32_t *status,
+               void *stream);
+
 /* Status word kept in the workspace: bit 0 set when a kernel met a record
  * descriptor outside the pool or with tag 3 (that expert was skipped; its
  * contribution is zero); bit 2 set when the decode kernel's bounded wait for

@@ -83,10 +83,13 @@ def _load():
     lib.moe_prefill_forward.argtypes = [vp, ctypes.c_int32, P(MoeRouter), P(MoePrefillPlan),
                                         P(MoePool), P(MoeShared), vp, vp]
     lib.moe_workspace_status.argtypes = [vp, ctypes.c_size_t, vp]
+    lib.moe_repack.argtypes = [vp, ctypes.c_uint64, vp, vp, ctypes.c_uint64, vp, ctypes.c_int32,
+                               ctypes.c_int32, ctypes.c_int32, vp, vp]
     lib.moe_set_stage_events.argtypes = [P(ctypes.c_void_p), ctypes.c_int32]
     lib.moe_last_error.restype = ctypes.c_char_p
     for name in ("moe_set_stage_events", "moe_workspace_init", "moe_route", "moe_layer_forward",
-                 "moe_layer_forward_noalloc", "moe_prefill_forward", "moe_workspace_status"):
+                 "moe_layer_forward_noalloc", "moe_prefill_forward", "moe_workspace_status",
+                 "moe_repack"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -172,6 +175,15 @@ def layer_forward_noalloc(x, nb: int, router: MoeRouter, slots: MoeSlots, pool: 
     _check(lib.moe_layer_forward_noalloc(_ptr(x), nb, ctypes.byref(router), ctypes.byref(slots),
                                          ctypes.byref(pool), ctypes.byref(shared), _ptr(out),
                                          _stream(stream)))
+
+
+def repack(src_pool, src_desc, dst_pool, dst_desc, n: int, hidden: int, inter: int,
+           status=None, stream=None) -> None:
+    """moe_repack: 4-bit records at src_desc[:n] requantized into the widths
+    and offsets dst_desc[:n] name (device tensors)."""
+    _check(lib.moe_repack(_ptr(src_pool), src_pool.numel(), _ptr(src_desc), _ptr(dst_pool),
+                          dst_pool.numel(), _ptr(dst_desc), n, hidden, inter, _ptr(status),
+                          _stream(stream)))
 
 
 def static_scratch_status(stream=None) -> int:

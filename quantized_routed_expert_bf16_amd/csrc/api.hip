@@ -392,6 +392,25 @@ int moe_prefill_forward(const float *x, int32_t t, const moe_router *router, moe
   return rc ? rc : ok();
 }
 
+int moe_repack(const uint8_t *src_pool, uint64_t src_bytes, const uint64_t *src_desc, uint8_t *dst_pool,
+               uint64_t dst_bytes, const uint64_t *dst_desc, int32_t n_records, int32_t hidden, int32_t inter,
+               uint32_t *status, void *stream) {
+  moe_dims d{hidden, inter, 1, 1};
+  int rc = check_dims(&d);
+  if (rc) return rc;
+  if (n_records < 0) return fail(MOE_EINVAL, "n_records %d: must be >= 0", n_records);
+  if (n_records == 0) return ok();
+  REQ(src_pool, 256, "src_pool");
+  REQ(dst_pool, 256, "dst_pool");
+  REQ(src_desc, 8, "src_desc");
+  REQ(dst_desc, 8, "dst_desc");
+  if (status && !aligned(status, 4)) return fail(MOE_EINVAL, "status is not 4-byte aligned");
+  rc = launched(launch_repack(src_pool, src_bytes, src_desc, dst_pool, dst_bytes, dst_desc, n_records, hidden,
+                              inter, status, static_cast<hipStream_t>(stream)),
+                "repack");
+  return rc ? rc : ok();
+}
+
 int moe_workspace_status(void *ws, size_t ws_bytes, void *stream) {
   if (!ws && ws_bytes == 0) {   // the static scratch of moe_layer_forward_noalloc on this device
     ws = scratch_if_set_up();

@@ -85,7 +85,7 @@ def record_bytes(hidden: int, inter: int, bits: int) -> int:
 
 def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
     """Pack integer codes [rows][n] into bytes [rows][n*bits/8]."""
-    codes = np.asarray(codes, dtype=np.uint64)
+    codes = np.ascontiguousarray(codes, dtype=np.uint64)
     rows, n = codes.shape
     assert n % GROUP == 0 and codes.max(initial=0) < (1 << bits)
     if bits in (4, 2):
