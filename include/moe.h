@@ -168,6 +168,116 @@ int moe_layer_forward(const float *x, int32_t nb, const moe_router *router,
                       moe_slots *slots, const moe_pool *pool,
                       const moe_shared *shared, float *out, void *stream);
 
+/* One part of the experts of a slot table the caller published (Struct Gpu
+ * experts_b; the slot_tab field doc: entry 62 = resident count, 63 = union
+ * size).  part 0 runs the union slots [0, tab[62]) -- the records resident
+ * when the table was published -- plus the shared expert (weight gamma[b]),
+ * and overwrites out; part 1 runs the slots [tab[62], tab[63]) -- the
+ * records fetched meanwhile -- and adds them to out.  Between the two the
+ * caller may fill the late records' pool bytes (for example copies from a
+ * host tier ordered before part 1 on `stream`).
+ *   slots->tab: device [64] descriptors as published (entries j < tab[63]
+ *     name records in the pool; 0 <= tab[62] <= tab[63] <= 62, else the
+ *     counts are clamped and status bit 0 is set); slots->wmap: device
+ *     [4][64] per-row weights of the published slots; slots->gamma: device
+ *     [nb] shared gate values (as moe_route writes them); slots->ws as for
+ *     moe_layer_forward.  ids, topk_idx, topk_w and logits are not used.
+ *   out: device f32 [nb][H]; x: device f32 [nb][H]; dims: host.
+ * A record the table names that lies outside the pool is skipped (zero
+ * contribution) and flags status bit 0. */
+int moe_experts_part(const float *x, int32_t nb, const moe_dims *dims, moe_slots *slots,
+                     int32_t part, const moe_pool *pool, const moe_shared *shared, float *out,
+                     void *stream);
+
+/* ------------------------------------------------------------------------
+ * Two-part dispatch over a host-pinned record tier.  The pages' engine keeps
+ * every expert record outside GPU memory and a fixed pool of device slots,
+ * LRU managed (gpu.rs module doc; Struct Gpu: res, event, event_res,
+ * service_block, experts_b).  Per layer: the GPU routes and the CPU reads
+ * the union; the CPU publishes the slot table with the resident records
+ * first (entry 62 = resident count, 63 = union size); part 0 (resident
+ * records + shared expert) runs while the CPU copies the missing records
+ * into free slots; part 1 runs once they have landed.  Here the store is
+ * pinned host memory the caller fills, the copies run on a second stream,
+ * and the GPU<->CPU signals are stream synchronisation and HIP events.
+ * Two policies of the pages are options: the deadline cut of weak late
+ * records (Struct Gpu cut_w, wait_for_deadline) and the one-layer
+ * lookahead prefetch (Struct Gpu lookahead_layer, prefetch_async,
+ * lookahead_hit).  The tier object is host memory plus a small pinned
+ * staging area and one HIP event per slot, created by moe_tier_create and
+ * released by moe_tier_destroy; device memory is the caller's.
+ * ---------------------------------------------------------------------- */
+typedef struct moe_tier moe_tier;
+
+typedef struct moe_tier_config {
+    moe_dims dims;
+    int32_t n_layers;
+    const uint8_t *host_tier;    /* pinned host memory (hipHostMalloc) holding every routed record */
+    uint64_t host_bytes;
+    const uint64_t *host_desc;   /* host [n_layers][E]: descriptor of record (layer, expert) in the
+                                    host tier (offset | bits tag) */
+    uint8_t *dev_pool;           /* device pool: the slot region, plus whatever else the caller keeps
+                                    there (the shared experts' records) */
+    uint64_t dev_bytes;
+    uint64_t slot_offset;        /* byte offset of slot 0 in dev_pool (multiple of 256) */
+    uint64_t slot_stride;        /* bytes per slot: >= a 4-bit record, multiple of 256 */
+    int32_t n_slots;             /* >= k * MAX_NB, so that a whole union fits */
+} moe_tier_config;
+
+typedef struct moe_tier_policy {
+    float cut_w;            /* > 0: at the deadline (part 0 done) a fetched record whose weight is
+                               below cut_w in every row and whose copy has not landed is cut from
+                               part 1 (its copy still completes); 0 = off */
+    int32_t deadline_now;   /* 1: no fetched record counts as landed at the deadline (a
+                               deterministic cut set, for tests and error studies) */
+    int32_t lookahead;      /* 1: the next layer's router runs on this layer's input and the
+                               records it predicts are fetched after this layer's copies */
+    int32_t timing;         /* 1: fill part0_us and fetch_us (synchronises the streams) */
+} moe_tier_policy;
+
+typedef struct moe_tier_stats {
+    int32_t n_union;        /* union size of this layer's step */
+    int32_t n_resident;     /* records resident when the table was published (part 0) */
+    int32_t n_fetched;      /* records copied from the host tier for part 1 */
+    int32_t n_cut;          /* fetched records cut at the deadline */
+    int32_t n_prefetched;   /* records fetched for the next layer by the lookahead */
+    int32_t n_predicted;    /* experts the previous call predicted for this layer */
+    int32_t n_hit;          /* of this layer's union, how many were predicted */
+    float part0_us;         /* part 0 kernel time (timing = 1) */
+    float fetch_us;         /* copy-stream time of this layer's fetches (timing = 1) */
+} moe_tier_stats;
+
+/* Validates the configuration (every host descriptor inside the host tier)
+ * and creates the tier; the slots start empty.  MOE_EINVAL with a message
+ * (moe_tier_last_error) on a bad configuration, MOE_ELAUNCH on a HIP error. */
+int moe_tier_create(const moe_tier_config *cfg, moe_tier **out);
+void moe_tier_destroy(moe_tier *t);
+
+/* Copy the records of `experts` (n ids) of `layer` into free or least
+ * recently used slots on copy_stream (warming the pool).  Call only while
+ * no kernel reads the slots. */
+int moe_tier_warm(moe_tier *t, int32_t layer, const int32_t *experts, int32_t n, void *copy_stream);
+
+/* One MoE layer through the tier: moe_route on `stream` (router->rec may be
+ * any device array of E descriptors: its slot table output is replaced),
+ * the handshake, the published table in slots->tab / wmap / ids (resident
+ * first), part 0, the copies on copy_stream, optionally the deadline cut
+ * and the lookahead (next_router: the next layer's router; la_slots: its own
+ * result buffers, which may share slots->ws), part 1.  out: device f32
+ * [nb][H], overwritten.  Returns after part 1 is enqueued; the host blocks
+ * on the route (and on part 0 when cut_w > 0, and on the lookahead route).
+ * Errors are reported with moe_tier_last_error. */
+int moe_tier_layer(moe_tier *t, int32_t layer, const float *x, int32_t nb, const moe_router *router,
+                   moe_slots *slots, const moe_shared *shared, float *out,
+                   const moe_tier_policy *policy, const moe_router *next_router,
+                   moe_slots *la_slots, moe_tier_stats *stats, void *stream, void *copy_stream);
+
+/* `stream` waits for every copy issued so far (cut or prefetched records). */
+int moe_tier_join(moe_tier *t, void *stream);
+
+/* Text of the last tier error on the calling thread. */
+const char *moe_tier_last_error(void);
+
 /* moe_layer_forward for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  Same arguments, kernels and results as moe_layer_forward,

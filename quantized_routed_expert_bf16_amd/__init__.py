@@ -64,6 +64,29 @@ class MoePrefillPlan(ctypes.Structure):
                 ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
 
 
+class MoeTierConfig(ctypes.Structure):
+    _fields_ = [("dims", MoeDims), ("n_layers", ctypes.c_int32), ("host_tier", ctypes.c_void_p),
+                ("host_bytes", ctypes.c_uint64), ("host_desc", ctypes.c_void_p),
+                ("dev_pool", ctypes.c_void_p), ("dev_bytes", ctypes.c_uint64),
+                ("slot_offset", ctypes.c_uint64), ("slot_stride", ctypes.c_uint64),
+                ("n_slots", ctypes.c_int32)]
+
+
+class MoeTierPolicy(ctypes.Structure):
+    _fields_ = [("cut_w", ctypes.c_float), ("deadline_now", ctypes.c_int32),
+                ("lookahead", ctypes.c_int32), ("timing", ctypes.c_int32)]
+
+
+class MoeTierStats(ctypes.Structure):
+    _fields_ = [("n_union", ctypes.c_int32), ("n_resident", ctypes.c_int32),
+                ("n_fetched", ctypes.c_int32), ("n_cut", ctypes.c_int32),
+                ("n_prefetched", ctypes.c_int32), ("n_predicted", ctypes.c_int32),
+                ("n_hit", ctypes.c_int32), ("part0_us", ctypes.c_float), ("fetch_us", ctypes.c_float)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
@@ -80,6 +103,8 @@ def _load():
     lib.moe_layer_forward.argtypes = [vp, ctypes.c_int32, P(MoeRouter), P(MoeSlots), P(MoePool),
                                       P(MoeShared), vp, vp]
     lib.moe_layer_forward_noalloc.argtypes = lib.moe_layer_forward.argtypes
+    lib.moe_experts_part.argtypes = [vp, ctypes.c_int32, P(MoeDims), P(MoeSlots), ctypes.c_int32,
+                                     P(MoePool), P(MoeShared), vp, vp]
     lib.moe_prefill_forward.argtypes = [vp, ctypes.c_int32, P(MoeRouter), P(MoePrefillPlan),
                                         P(MoePool), P(MoeShared), vp, vp]
     lib.moe_workspace_status.argtypes = [vp, ctypes.c_size_t, vp]
@@ -87,9 +112,19 @@ def _load():
                                ctypes.c_int32, ctypes.c_int32, vp, vp]
     lib.moe_set_stage_events.argtypes = [P(ctypes.c_void_p), ctypes.c_int32]
     lib.moe_last_error.restype = ctypes.c_char_p
+    lib.moe_tier_create.argtypes = [P(MoeTierConfig), P(ctypes.c_void_p)]
+    lib.moe_tier_destroy.argtypes = [vp]
+    lib.moe_tier_destroy.restype = None
+    lib.moe_tier_warm.argtypes = [vp, ctypes.c_int32, vp, ctypes.c_int32, vp]
+    lib.moe_tier_layer.argtypes = [vp, ctypes.c_int32, vp, ctypes.c_int32, P(MoeRouter), P(MoeSlots),
+                                   P(MoeShared), vp, P(MoeTierPolicy), P(MoeRouter), P(MoeSlots),
+                                   P(MoeTierStats), vp, vp]
+    lib.moe_tier_join.argtypes = [vp, vp]
+    lib.moe_tier_last_error.restype = ctypes.c_char_p
     for name in ("moe_set_stage_events", "moe_workspace_init", "moe_route", "moe_layer_forward",
                  "moe_layer_forward_noalloc", "moe_prefill_forward", "moe_workspace_status",
-                 "moe_repack"):
+                 "moe_repack", "moe_experts_part", "moe_tier_create", "moe_tier_warm",
+                 "moe_tier_layer", "moe_tier_join"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -175,6 +210,14 @@ def layer_forward_noalloc(x, nb: int, router: MoeRouter, slots: MoeSlots, pool: 
     _check(lib.moe_layer_forward_noalloc(_ptr(x), nb, ctypes.byref(router), ctypes.byref(slots),
                                          ctypes.byref(pool), ctypes.byref(shared), _ptr(out),
                                          _stream(stream)))
+
+
+def experts_part(x, nb: int, dims: MoeDims, slots: MoeSlots, part: int, pool: MoePool,
+                 shared: MoeShared, out, stream=None) -> None:
+    """moe_experts_part: part 0 (resident slots + shared, overwrites out) or
+    part 1 (fetched slots, adds to out) of the table in slots.tab / wmap."""
+    _check(lib.moe_experts_part(_ptr(x), nb, ctypes.byref(dims), ctypes.byref(slots), part,
+                                ctypes.byref(pool), ctypes.byref(shared), _ptr(out), _stream(stream)))
 
 
 def repack(src_pool, src_desc, dst_pool, dst_desc, n: int, hidden: int, inter: int,
@@ -284,3 +327,61 @@ class PrefillBuffers:
                                    self.logits.data_ptr(), self.gamma.data_ptr(),
                                    self.expert_ptr.data_ptr(), self.entry_row.data_ptr(),
                                    self.entry_rank.data_ptr(), self.ws.data_ptr(), nbytes)
+
+
+class Tier:
+    """A moe_tier over a pinned host tier (torch pin_memory tensor, which
+    torch allocates with hipHostMalloc) and a device pool; the binding only
+    passes pointers and keeps the tensors alive."""
+
+    def __init__(self, dims: MoeDims, n_layers: int, host_tier: torch.Tensor,
+                 host_desc, dev_pool: torch.Tensor, slot_offset: int, slot_stride: int,
+                 n_slots: int):
+        assert host_tier.is_pinned() and host_tier.dtype == torch.uint8
+        import numpy as np
+        self._desc = np.ascontiguousarray(np.asarray(host_desc, dtype=np.uint64).reshape(-1))
+        self._keep = (host_tier, dev_pool)
+        self.cfg = MoeTierConfig(dims, n_layers, host_tier.data_ptr(), host_tier.numel(),
+                                 self._desc.ctypes.data, dev_pool.data_ptr(), dev_pool.numel(),
+                                 slot_offset, slot_stride, n_slots)
+        h = ctypes.c_void_p()
+        rc = lib.moe_tier_create(ctypes.byref(self.cfg), ctypes.byref(h))
+        if rc:
+            raise MoeError(rc, lib.moe_tier_last_error().decode())
+        self.handle = h.value
+        self.copy_stream = torch.cuda.Stream()
+
+    def _chk(self, rc):
+        if rc:
+            raise MoeError(rc, lib.moe_tier_last_error().decode())
+
+    def warm(self, layer: int, experts) -> None:
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(experts, dtype=np.int32))
+        self._chk(lib.moe_tier_warm(self.handle, layer, ids.ctypes.data, ids.size,
+                                    self.copy_stream.cuda_stream))
+        self.copy_stream.synchronize()
+
+    def layer(self, layer: int, x, nb: int, router: MoeRouter, slots: MoeSlots,
+              shared: MoeShared, out, policy: MoeTierPolicy | None = None,
+              next_router: MoeRouter | None = None, la_slots: MoeSlots | None = None,
+              stream=None) -> dict:
+        st = MoeTierStats()
+        self._chk(lib.moe_tier_layer(self.handle, layer, _ptr(x), nb, ctypes.byref(router),
+                                     ctypes.byref(slots), ctypes.byref(shared), _ptr(out),
+                                     ctypes.byref(policy) if policy is not None else None,
+                                     ctypes.byref(next_router) if next_router is not None else None,
+                                     ctypes.byref(la_slots) if la_slots is not None else None,
+                                     ctypes.byref(st), _stream(stream), self.copy_stream.cuda_stream))
+        return st.as_dict()
+
+    def join(self, stream=None) -> None:
+        self._chk(lib.moe_tier_join(self.handle, _stream(stream)))
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            lib.moe_tier_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        self.close()

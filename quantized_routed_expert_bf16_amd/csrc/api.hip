@@ -392,6 +392,28 @@ int moe_prefill_forward(const float *x, int32_t t, const moe_router *router, moe
   return rc ? rc : ok();
 }
 
+int moe_experts_part(const float *x, int32_t nb, const moe_dims *dims, moe_slots *slots, int32_t part,
+                     const moe_pool *pool, const moe_shared *shared, float *out, void *stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (nb < 1 || nb > MOE_MAX_NB) return fail(MOE_EINVAL, "nb %d: must be in 1..%d", nb, MOE_MAX_NB);
+  if (part != 0 && part != 1) return fail(MOE_EINVAL, "part %d: must be 0 or 1", part);
+  REQ(x, 16, "x");
+  REQ(out, 16, "out");
+  if ((rc = check_pool(pool))) return rc;
+  if ((rc = check_shared(shared, *dims, pool))) return rc;
+  if (!slots) return fail(MOE_EINVAL, "slots is NULL");
+  REQ(slots->tab, 8, "slots.tab");
+  REQ(slots->wmap, 4, "slots.wmap");
+  REQ(slots->gamma, 4, "slots.gamma");
+  if ((rc = check_ws(slots->ws, slots->ws_bytes, *dims, nb))) return rc;
+  moe_router r{};
+  r.dims = *dims;   // the router itself is not read: the table is published
+  const LayerLaunch l = layer_launch(x, nb, &r, slots, pool, shared, out, static_cast<uint8_t *>(slots->ws));
+  rc = launched(launch_layer(l, static_cast<hipStream_t>(stream), part), "experts part");
+  return rc ? rc : ok();
+}
+
 int moe_repack(const uint8_t *src_pool, uint64_t src_bytes, const uint64_t *src_desc, uint8_t *dst_pool,
                uint64_t dst_bytes, const uint64_t *dst_desc, int32_t n_records, int32_t hidden, int32_t inter,
                uint32_t *status, void *stream) {

@@ -70,6 +70,7 @@ struct LayerArgs {
   int per_slice;     // blocks per slice (gridDim.x / 8)
   int route_blocks;  // router blocks in all (block g = lr * n_slices + x)
   uint32_t d_codes[3], d_sb[3];   // down section offsets in a record, per bits tag 0..2
+  int part;          // -1: route and run every expert; 0 / 1: part of a published slot table
 };
 
 __device__ inline uint32_t *sw(const LayerArgs &a, int x, int field) {
@@ -114,6 +115,7 @@ struct Shared {
   int dbits[kSlotStride];               // bit width (0: bad descriptor)
   float gam[NB];
   int u;
+  int nsl;            // slots the down tiles take: u + 1 (the shared expert last), u in part 1
   uint32_t prev;
   uint32_t ep;        // this call's epoch
 };
@@ -394,7 +396,10 @@ __device__ __forceinline__ void route_union(const LayerArgs &a, Shared<NB> &s, c
     }
     const float w_l = ent ? ex / sum : 0.0f;
     if (ent) s.wsel[lb][lr] = w_l;
-    if (lane == 0) s.u = u;
+    if (lane == 0) {
+      s.u = u;
+      s.nsl = u + 1;
+    }
 #pragma unroll
     for (int b = 0; b < NB; ++b) s.wslot[b][lane] = lane == u ? s.gam[b] : 0.0f;
     __builtin_amdgcn_wave_barrier();
@@ -430,6 +435,50 @@ __device__ __forceinline__ void route_union(const LayerArgs &a, Shared<NB> &s, c
     }
     if (threadIdx.x < NB) a.l.gamma[threadIdx.x] = s.gam[threadIdx.x];
   }
+}
+
+// The slots of one part of a slot table published by the caller (Struct Gpu
+// experts_b: part 0 runs the records resident when the table was published,
+// entries [0, tab[62]), plus the shared expert; part 1 the records fetched
+// meanwhile, entries [tab[62], tab[63])), with the per-row weights of wmap
+// and the shared gate values in gamma.  Counts outside 0 <= tab[62] <=
+// tab[63] <= 62 are clamped and flag status bit 0.
+template <int NB>
+__device__ __forceinline__ void table_slots(const LayerArgs &a, Shared<NB> &s) {
+  const int j = threadIdx.x;
+  const uint64_t r62 = a.l.tab[MOE_RESIDENT_ENTRY], r63 = a.l.tab[MOE_UNION_ENTRY];
+  const int n_u = int(min(r63, uint64_t(MOE_RESIDENT_ENTRY)));
+  const int n_res = int(min(r62, uint64_t(n_u)));
+  const int begin = a.part == 0 ? 0 : n_res, end = a.part == 0 ? n_res : n_u;
+  const int u = end - begin;
+  const bool shared = a.part == 0;
+  if (j == 0 && (r62 > r63 || r63 > uint64_t(MOE_RESIDENT_ENTRY))) set_status(a, 1u);
+  if (j <= u && j < kSlotStride) {
+    const uint64_t d = j < u ? a.l.tab[begin + j] : (shared ? a.l.shared_rec : 0);
+    const bool ok = (j < u || shared) && record_ok(d, a.l.pool_bytes, a.l.hidden, a.l.inter);
+    const int bt = ok ? bits_of_tag(d) : 0;
+    const RecordLayout L = record_layout(a.l.hidden, a.l.inter, ok ? bt : 4);
+    const uint8_t *rec = a.l.pool + (d & ~uint64_t(255));
+    s.desc[j] = d;
+    s.dbits[j] = bt;
+    s.dcodes[j] = ok ? rec + L.d_codes : nullptr;
+    s.dsb[j] = ok ? reinterpret_cast<const uint32_t *>(rec + L.d_sb) : nullptr;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      s.wslot[b][j] = j < u ? a.l.wmap[b * kSlotStride + begin + j] : (shared ? a.l.gamma[b] : 0.0f);
+    if (j < u && !ok) set_status(a, 1u);
+  }
+  if (j == 0) {
+    s.u = u;
+    s.nsl = shared ? u + 1 : u;
+  }
+  __syncthreads();
+}
+
+template <int NB>
+__device__ __forceinline__ void build_slots(const LayerArgs &a, Shared<NB> &s, const uint64_t *rec_lds) {
+  if (a.part >= 0) table_slots<NB>(a, s);
+  else route_union<NB>(a, s, rec_lds);
 }
 
 // ------------------------------------------------------------ gate / up
@@ -928,7 +977,8 @@ __device__ __forceinline__ void combine_tile(const LayerArgs &a, const Shared<NB
 #pragma unroll
       for (int q = 0; q < kSlices; ++q)
         if (q < a.n_slices) v += __uint_as_float(uint32_t(w[q]));
-      a.l.out[size_t(b) * H + r] = v;
+      // part 1 adds to part 0's output (an earlier launch on the stream)
+      a.l.out[size_t(b) * H + r] = a.part == 1 ? a.l.out[size_t(b) * H + r] + v : v;
     }
   }
   __syncthreads();
@@ -968,7 +1018,7 @@ __device__ __forceinline__ void down_load(const LayerArgs &a, const Shared<NB> &
   const int row = tile * kRowsPerTile + wave * kRowsPerWave + rw;
   const int col = x * W + c * kChunk;
   const int grp = col / kGroup, half = (col % kGroup) / kChunk;
-  const int n_slots = sh.u + 1;
+  const int n_slots = sh.nsl;
   // section offsets read with constant indices (scalar loads of the kernel
   // arguments), then chosen per lane by the bits tag
   const uint32_t dc0 = a.d_codes[0], dc1 = a.d_codes[1], dc2 = a.d_codes[2];
@@ -1005,7 +1055,7 @@ __device__ __forceinline__ void run_down(const LayerArgs &a, Shared<NB> &sh, int
   const int sg = 8 / cpr;                     // slot groups per row
   const int idx = lane & 7;
   const int c = idx % cpr, g = idx / cpr;
-  const int u = sh.u, n_slots = u + 1;
+  const int u = sh.u, n_slots = sh.nsl;
   constexpr int kSB = slot_batch<NB>();
   float acc[NB];
 #pragma unroll
@@ -1138,7 +1188,7 @@ __device__ __forceinline__ void run_down_m(const LayerArgs &a, Shared<NB> &sh, i
   const int q = lane >> 4, j = lane & 15;
   const int rb = wave & 1, par = wave >> 1;
   const int r0 = tile * kRowsPerTile + 16 * rb;   // the wave's 16 rows
-  const int u = sh.u, n_slots = u + 1;
+  const int u = sh.u, n_slots = sh.nsl;
   floatx4 tot = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int s0 = 0; s0 < n_slots; s0 += 2 * kDownSlots) {
     // 1. the lane's code words and the (scale, bias) words of its 4 output
@@ -1374,7 +1424,9 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
 
 
   if (x < a.n_slices) {
-    // router blocks g < G are spread over the slices; R of them are in this one
+    // router blocks g < G are spread over the slices; R of them are in this
+    // one (none for a part of a published table: route_blocks is 0)
+    const bool tbl = a.part >= 0;
     const int g = lr * a.n_slices + x;
     const bool route = g < a.route_blocks;
     const int R = x < a.route_blocks ? (a.route_blocks - 1 - x) / a.n_slices + 1 : 0;
@@ -1382,8 +1434,8 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
     if (route) router_prefetch<CPL>(a, g, rrow);
     // the descriptors go to LDS with x, so that no wait for them holds up
     // the x loads
-    const uint64_t rv = a.l.rec[min(int(threadIdx.x), a.l.n_experts - 1)];
-    stage_x<NB, CPL>(a, xs, xsum, rec_lds, rv, &sh.ep);
+    const uint64_t rv = tbl ? 0 : a.l.rec[min(int(threadIdx.x), a.l.n_experts - 1)];
+    stage_x<NB, CPL>(a, xs, xsum, tbl ? nullptr : rec_lds, rv, &sh.ep);
 
     double *lg = a.l.slice_logits;
     float *gm = a.l.slice_gamma;
@@ -1400,19 +1452,22 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
       stage_x_fragments<NB>(a, xs, xsum, xb, xg);
       __syncthreads();
     }
-    // the shared expert's gate/up units need no routing
-    for (int i = ((lr - R) % P + P) % P; i < a.ups; i += P)
+    // the shared expert's gate/up units need no routing (part 1 has none)
+    const int shared_units = a.part == 1 ? 0 : a.ups;
+    for (int i = ((lr - R) % P + P) % P; i < shared_units; i += P)
       gate_up_item<NB, CPL, kM>(a, x, a.l.shared_rec, kSharedSlot, i, xs, xsum, xb, xg, red, sh.ep);
 
-    wait_geq(a, sw(a, x, kSliceRoute), uint32_t(a.route_blocks));
-    route_select<NB>(a, sh, lg, gm);
+    if (!tbl) {
+      wait_geq(a, sw(a, x, kSliceRoute), uint32_t(a.route_blocks));
+      route_select<NB>(a, sh, lg, gm);
+    }
     // the block's work items i0, i0 + P, ...: gate/up units first, then down
     // tiles (two loops, so neither carries the other's live values).  When
     // the first unit's slot is one of row 0's ranks its expert is known
     // already: its weights load while the union is built.
     int i = ((lr - R - a.ups) % P + P) % P;
     const int slot0 = i / a.ups;
-    const bool early = slot0 < a.l.top_k;
+    const bool early = !tbl && slot0 < a.l.top_k;
     uint64_t d0 = 0;
     if (early) d0 = rec_lds[sh.sel[0][slot0]];
     if constexpr (kM) {
@@ -1425,7 +1480,7 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
       const bool em = early && bits_of_tag(d0) == 4 && record_ok(d0, a.l.pool_bytes, a.l.hidden, a.l.inter);
       if (em) gate_up_load_m<4>(a, d0, x, i - slot0 * a.ups, cur);
       asm volatile("" ::: "memory");   // the loads are issued here, not sunk to their use
-      route_union<NB>(a, sh, rec_lds);
+      build_slots<NB>(a, sh, rec_lds);
       const int n_gu0 = sh.u * a.ups;
       auto load_unit = [&](int it, GuRegsM &r) {
         const int slot = it / a.ups;
@@ -1458,7 +1513,7 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
       if (early && record_ok(d0, a.l.pool_bytes, a.l.hidden, a.l.inter))
         gate_up_load_any<CPL>(a, d0, gate_up_row0(a, x, i - slot0 * a.ups), pre);
       asm volatile("" ::: "memory");   // the loads are issued here, not sunk to their use
-      route_union<NB>(a, sh, rec_lds);
+      build_slots<NB>(a, sh, rec_lds);
       const int n_gu = sh.u * a.ups;
       if (early) {   // slot0 < k <= u: a gate/up unit
         run_gate_up<NB, CPL, true>(a, x, d0, slot0, i - slot0 * a.ups, xs, xsum, sh.ep, pre);
@@ -1569,7 +1624,7 @@ hipError_t launch_nb(LayerArgs &a, hipStream_t s) {
   }
   const int grid = (per_cu * g_cache.cus) / kSlices * kSlices;
   a.per_slice = grid / kSlices;
-  a.route_blocks = min(a.per_slice * a.n_slices, (a.l.n_experts + 1 + kWaves - 1) / kWaves);
+  a.route_blocks = a.part >= 0 ? 0 : min(a.per_slice * a.n_slices, (a.l.n_experts + 1 + kWaves - 1) / kWaves);
   hipLaunchKernelGGL((layer_kernel<NB, CPL, kM>), dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
@@ -1587,6 +1642,7 @@ hipError_t launch_route_nb(LayerArgs &a, hipStream_t s) {
 hipError_t launch_route_only(const LayerLaunch &l, hipStream_t s) {
   LayerArgs a{};
   a.l = l;
+  a.part = -1;
   a.n_slices = 1;
   a.route_blocks = (l.n_experts + 1 + kWaves - 1) / kWaves;
   a.per_slice = a.route_blocks;
@@ -1599,9 +1655,10 @@ hipError_t launch_route_only(const LayerLaunch &l, hipStream_t s) {
   }
 }
 
-hipError_t launch_layer(const LayerLaunch &l, hipStream_t s) {
+hipError_t launch_layer(const LayerLaunch &l, hipStream_t s, int part) {
   LayerArgs a{};
   a.l = l;
+  a.part = part;
   a.n_slices = min(kSlices, l.inter / kChunk);
   a.W = l.inter / a.n_slices;
   a.ups = a.W / kTileRowPairs;

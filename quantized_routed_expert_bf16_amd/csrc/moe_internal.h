@@ -106,7 +106,8 @@ constexpr int kMaxDownTiles = 256;
 
 // ------------------------------------------------------------- launchers
 hipError_t launch_route_only(const LayerLaunch &l, hipStream_t s);   // moe_route
-hipError_t launch_layer(const LayerLaunch &l, hipStream_t s);
+// part -1: route and run the layer; 0 / 1: a part of the published slot table
+hipError_t launch_layer(const LayerLaunch &l, hipStream_t s, int part = -1);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_repack(const uint8_t *src, uint64_t src_bytes, const uint64_t *src_desc, uint8_t *dst,
                          uint64_t dst_bytes, const uint64_t *dst_desc, int n, int hidden, int inter,
