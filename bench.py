@@ -129,7 +129,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="decode_nb1")
-    ap.add_argument("--extra", default="verify_nb4,lowbit_q3,lowbit_q2,mixed_q4q2,prefill_t32,repack",
+    ap.add_argument("--extra", default="verify_nb4,lowbit_q3,lowbit_q2,mixed_q4q2,prefill_t32,repack,tier",
                     help="comma-separated further configurations reported under 'extra'")
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
     ap.add_argument("--chunk", type=int, default=25, help="steps per captured graph")
@@ -575,6 +575,132 @@ def bench_repack(moe, torch, syn, args):
     return out
 
 
+def bench_tier(moe, torch, syn, args):
+    """Two-part dispatch over a pinned host tier at full shape (hidden 2048,
+    width 512, 128 experts, top-8, nb = 1): 8 layers of 4-bit records in
+    pinned host memory, a device pool holding a fraction of them, inputs
+    correlated across layers (layer l + 1's input = RMS(x_l + 0.5 N(0,1))).
+    Host wall time per layer, part 0 and copy time, records fetched, the
+    lookahead's hit rate, and the deadline cut's effect on the output (the
+    cut output against moe_layer_forward's on the same input)."""
+    import numpy as np
+    cfg = syn.CONFIGS["decode_nb1"]
+    H, I, E, k = cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k
+    L, steps, rho = 8, 4, 0.5
+    p = syn.make_problem(cfg, seed=args.seed, device="cuda", n_layers=L)
+    routed_bytes = int(p.shared_rec[0]) & ~0xFF
+    host = torch.empty(routed_bytes, dtype=torch.uint8, pin_memory=True)
+    host.copy_(p.pool[:routed_bytes])
+    rb4 = moe.record_bytes(H, I, 4)
+    dims = moe.make_dims(H, I, E, k)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(args.seed + 5)
+    x = torch.randn(steps, L, 1, H, device="cuda", generator=g)
+    for l in range(1, L):
+        x[:, l] = x[:, l - 1] + rho * x[:, l]
+    x = (x / torch.sqrt((x * x).mean(dim=-1, keepdim=True))).contiguous()
+    routers = [moe.make_router(dims, p.router[l], p.rec[l]) for l in range(L)]
+    out = torch.zeros(1, H, dtype=torch.float32, device="cuda")
+    bufs, la = moe.DecodeBuffers(dims), moe.DecodeBuffers(dims)
+    res = {"config": "tier", "layers": L, "steps": steps, "rho": rho, "nb": 1,
+           "description": "decode nb=1 records in a pinned host tier, device pool of a fraction of them"}
+    for frac in (0.25, 1.0):
+        n_slots = int(frac * L * E)
+        dev = torch.zeros(n_slots * rb4 + L * rb4, dtype=torch.uint8, device="cuda")
+        shared = []
+        for l in range(L):
+            off = n_slots * rb4 + l * rb4
+            so = int(p.shared_rec[l]) & ~0xFF
+            dev[off: off + rb4] = p.pool[so: so + rb4]
+            shared.append(moe.make_shared(p.shared_gate[l], off))
+        for mode in ("plain", "lookahead"):
+            tier = moe.Tier(dims, L, host, p.rec.cpu().numpy(), dev, 0, rb4, n_slots)
+            # the pool starts warm with a seeded `frac` of every layer's experts
+            wg = np.random.default_rng(args.seed + 9)
+            for l in range(L):
+                tier.warm(l, np.sort(wg.permutation(E)[: int(frac * E)]))
+            pol = moe.MoeTierPolicy(0.0, 0, 1 if mode == "lookahead" else 0, 1)
+            walls, p0, fetch_us, fetched, hit, union, pred = [], [], [], [], 0, 0, 0
+            for st_i in range(steps):
+                for l in range(L):
+                    t0 = time.perf_counter()
+                    st = tier.layer(l, x[st_i, l], 1, routers[l], bufs.slots, shared[l], out, policy=pol,
+                                    next_router=routers[l + 1] if mode == "lookahead" and l + 1 < L else None,
+                                    la_slots=la.slots if mode == "lookahead" else None)
+                    torch.cuda.synchronize()
+                    if st_i > 0:   # after one step of lookahead history
+                        walls.append((time.perf_counter() - t0) * 1e6)
+                        p0.append(st["part0_us"])
+                        fetched.append(st["n_fetched"])
+                        if st["n_fetched"]:
+                            fetch_us.append(st["fetch_us"])
+                        if l > 0 and mode == "lookahead":
+                            hit += st["n_hit"]
+                            union += st["n_union"]
+                tier.join()
+            check_status(moe, bufs.ws, f"tier {frac} {mode}")
+            key = f"pool_{int(frac * 100)}pct_{mode}"
+            res[key] = {"n_slots": n_slots, "wall_us_per_layer_median": statistics.median(walls),
+                        "part0_us_median": statistics.median(p0),
+                        "fetched_per_layer_mean": float(np.mean(fetched)),
+                        "fetch_us_per_layer_median": statistics.median(fetch_us) if fetch_us else 0.0}
+            if mode == "lookahead":
+                res[key]["lookahead_hit_rate"] = hit / max(union, 1)
+            log(f"tier pool {int(frac * 100)}% {mode}: {res[key]}")
+            tier.close()
+        if frac == 0.25:
+            # deadline cut with every fetched record late (deadline_now): the
+            # output change against the full layer, per cut weight
+            study = {}
+            for cut_w in (0.05, 0.08, 0.1):
+                tier = moe.Tier(dims, L, host, p.rec.cpu().numpy(), dev, 0, rb4, n_slots)
+                wg = np.random.default_rng(args.seed + 9)
+                for l in range(L):
+                    tier.warm(l, np.sort(wg.permutation(E)[: int(frac * E)]))
+                pol = moe.MoeTierPolicy(cut_w, 1, 0, 0)
+                ref_bufs = moe.DecodeBuffers(dims)
+                pool_all = moe.make_pool(p.pool)
+                ref_shared = [moe.make_shared(p.shared_gate[l], int(p.shared_rec[l])) for l in range(L)]
+                ref = torch.zeros(1, H, dtype=torch.float32, device="cuda")
+                changes, cuts, fetches = [], 0, 0
+                for l in range(L):
+                    st = tier.layer(l, x[0, l], 1, routers[l], bufs.slots, shared[l], out, policy=pol)
+                    moe.layer_forward(x[0, l], 1, routers[l], ref_bufs.slots, pool_all, ref_shared[l], ref)
+                    torch.cuda.synchronize()
+                    a, b = out.cpu().numpy(), ref.cpu().numpy()
+                    changes.append(float(np.abs(a - b).max() / np.abs(b).max()))
+                    cuts += st["n_cut"]
+                    fetches += st["n_fetched"]
+                tier.join()
+                tier.close()
+                study[str(cut_w)] = {"cut_per_layer": cuts / L, "fetched_per_layer": fetches / L,
+                                     "max_change_over_max_out_median": statistics.median(changes),
+                                     "max_change_over_max_out_max": max(changes)}
+                log(f"tier cut_w {cut_w}: {study[str(cut_w)]}")
+            res["deadline_cut_study"] = study
+    # parity of one layer through the tier against the oracle (sampled)
+    import oracle.moe_oracle as mo
+    tier = moe.Tier(dims, L, host, p.rec.cpu().numpy(), dev, 0, rb4, L * E)
+    tier.layer(3, x[1, 3], 1, routers[3], bufs.slots, shared[3], out)
+    torch.cuda.synchronize()
+    u16 = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    class _Slices:
+        def __getitem__(self, sl):
+            return p.pool[sl].cpu().numpy()
+
+    r = mo.layer_forward(x[1, 3].cpu().numpy(), u16(p.router[3]), p.rec[3].cpu().numpy(), _Slices(),
+                         u16(p.shared_gate[3]), int(p.shared_rec[3]), k, H, I)
+    rel = float(np.abs(out.cpu().numpy() - r["out_f64"]).max() / np.abs(r["out_f64"]).max())
+    if rel > PARITY_TOL:
+        raise SystemExit(f"tier parity sample failed: {rel:.2e}")
+    res["parity_sampled"] = {"layers": 1, "max_err_over_absmax": rel}
+    tier.close()
+    del p, host, dev
+    torch.cuda.empty_cache()
+    return res
+
+
 def pct(v, q):
     v = sorted(v)
     return v[min(len(v) - 1, int(q * (len(v) - 1) + 0.5))]
@@ -774,6 +900,8 @@ def main():
     for name in [n for n in args.extra.split(",") if n]:
         if name == "repack":
             extra[name] = bench_repack(moe, torch, syn, args)
+        elif name == "tier":
+            extra[name] = bench_tier(moe, torch, syn, args)
         elif syn.CONFIGS[name].prefill:
             extra[name] = bench_prefill(moe, torch, syn, name, args)
         else:
