@@ -95,22 +95,37 @@ def blas_threads():
 
 
 def gpu_state():
-    """Clock and temperature of the GPU from rocm-smi (a separate process);
-    None where the tool is missing or its output has no such field."""
-    import subprocess
-    try:
-        r = subprocess.run(["rocm-smi", "--showtemp", "--showclocks", "--json"], capture_output=True,
-                           text=True, timeout=30)
-        data = json.loads(r.stdout)
-    except Exception as e:   # tool missing or no JSON: record why
-        return {"error": str(e)[:200]}
-    card = next((v for k, v in data.items() if k.startswith("card")), {})
-    keep = {}
-    for k, v in card.items():
-        kl = k.lower()
-        if "temperature" in kl or "sclk" in kl or "mclk" in kl or "fclk" in kl:
-            keep[k] = v
-    return keep
+    """Clock levels and temperatures of the GPUs, read from the amdgpu sysfs
+    files (no child process: a process that has opened the GPU must not start
+    programs); None fields where the files are missing."""
+    import glob
+    out = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            with open(dev + "/vendor") as f:
+                if f.read().strip() != "0x1002":
+                    continue
+        except OSError:
+            continue
+        card = {}
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk"):
+            try:
+                with open(f"{dev}/{name}") as f:   # the current level is marked with '*'
+                    cur = [l.strip() for l in f if "*" in l]
+                card[name] = cur[0] if cur else None
+            except OSError:
+                card[name] = None
+        temps = {}
+        for t in sorted(glob.glob(dev + "/hwmon/hwmon*/temp*_input")):
+            try:
+                label_path = t.replace("_input", "_label")
+                label = open(label_path).read().strip() if os.path.exists(label_path) else os.path.basename(t)
+                temps[label] = int(open(t).read().strip()) / 1000.0
+            except (OSError, ValueError):
+                pass
+        card["temp_c"] = temps or None
+        out[dev.split("/")[-2]] = card
+    return out or {"error": "no amdgpu sysfs entries"}
 
 
 def check_status(moe, ws, what):
