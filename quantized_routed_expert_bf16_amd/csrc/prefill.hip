@@ -686,21 +686,28 @@ __global__ __launch_bounds__(kThreads) void pf_down_kernel(PrefillArgs a) {
 }
 
 // ------------------------------------------------------------------ P5
-// Four columns a thread; all k + 1 rank rows are loaded before the sum,
-// which then runs in rank order (shared expert last).
-__global__ __launch_bounds__(kThreads) void pf_combine_kernel(PrefillArgs a) {
+// Four columns a thread, 64-thread blocks (the chunk's 256 KB of output
+// spread over every CU); all k + 1 rank rows are loaded before the sum (the
+// loads are unconditional, clamped to row k, so that none waits for the
+// previous one), which then runs in rank order (shared expert last).
+constexpr int kCombineThreads = 64;
+__global__ __launch_bounds__(kCombineThreads) void pf_combine_kernel(PrefillArgs a) {
   const int H = a.hidden, k = a.top_k;
-  for (int i = blockIdx.x * kThreads + threadIdx.x; i < a.t * H / 4; i += gridDim.x * kThreads) {
+  for (int i = blockIdx.x * kCombineThreads + threadIdx.x; i < a.t * H / 4; i += gridDim.x * kCombineThreads) {
     const int r = 4 * i / H, h = 4 * i - r * H;
     const float *y = a.y + size_t(r) * (k + 1) * H + h;
     float4 yv[kMaxTopK + 1];
 #pragma unroll
-    for (int c = 0; c <= kMaxTopK; ++c)
-      if (c <= k) yv[c] = *reinterpret_cast<const float4 *>(y + size_t(c) * H);
+    for (int c = 0; c <= kMaxTopK; ++c) yv[c] = *reinterpret_cast<const float4 *>(y + size_t(min(c, k)) * H);
     float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
-    for (int c = 0; c <= kMaxTopK; ++c)
-      if (c <= k) { v.x += yv[c].x; v.y += yv[c].y; v.z += yv[c].z; v.w += yv[c].w; }
+    for (int c = 0; c <= kMaxTopK; ++c) {
+      const bool on = c <= k;
+      v.x += on ? yv[c].x : 0.0f;
+      v.y += on ? yv[c].y : 0.0f;
+      v.z += on ? yv[c].z : 0.0f;
+      v.w += on ? yv[c].w : 0.0f;
+    }
     *reinterpret_cast<float4 *>(a.out + size_t(r) * H + h) = v;
   }
 }
@@ -734,8 +741,8 @@ hipError_t launch_prefill(const PrefillArgs &a, const uint16_t *router, const ui
   hipLaunchKernelGGL(pf_down_kernel, dim3(d_grid), dim3(kThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = mark(2)) != hipSuccess) return e;
-  const int c_grid = min((a.t * a.hidden / 4 + kThreads - 1) / kThreads, 1024);
-  hipLaunchKernelGGL(pf_combine_kernel, dim3(c_grid), dim3(kThreads), 0, s, a);
+  const int c_grid = min((a.t * a.hidden / 4 + kCombineThreads - 1) / kCombineThreads, 4096);
+  hipLaunchKernelGGL(pf_combine_kernel, dim3(c_grid), dim3(kCombineThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return mark(3);
 }
