@@ -56,6 +56,7 @@ constexpr int kStagePad = 4;                          // floats after each stage
 // staged act floats per row of x: (slot groups x kSlotBatch) runs of W + pad, W >= 32
 constexpr int kStageFloats = kStageCols * kSlotBatch + (kStageCols / kChunk) * kSlotBatch * kStagePad;
 constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr int kLateStageSleep = 20;   // s_sleep units (64 clocks each): ~0.5 us
 // x in LDS is chunk-major with rows of n_chunks + kXPad float4s: the pad
 // puts the 8 float4s of one chunk on different banks when they are written
 constexpr int kXPad = 1;
@@ -1432,6 +1433,11 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
     const int R = x < a.route_blocks ? (a.route_blocks - 1 - x) / a.n_slices + 1 : 0;
     RouterRow<CPL> rrow;
     if (route) router_prefetch<CPL>(a, g, rrow);
+    // Blocks that neither compute router rows nor run a shared-expert unit
+    // need x and the descriptors only after routing: they load them after a
+    // short sleep, so that the router blocks' loads of the same lines do not
+    // queue behind hundreds of identical requests.
+    if (!tbl && !route && ((lr - R) % P + P) % P >= a.ups) __builtin_amdgcn_s_sleep(kLateStageSleep);
     // the descriptors go to LDS with x, so that no wait for them holds up
     // the x loads
     const uint64_t rv = tbl ? 0 : a.l.rec[min(int(threadIdx.x), a.l.n_experts - 1)];
