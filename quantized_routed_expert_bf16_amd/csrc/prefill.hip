@@ -372,22 +372,23 @@ __device__ inline int entry_token_row(const PrefillArgs &a, const Job &j, int n)
 // B rows (f16 hi and lo halves, already in MFMA order), the tile's (scale,
 // bias) words and the B rows' group sums go straight from global memory into
 // LDS (global_load_lds: lane i's 16 or 4 bytes land at base + 16 i or 4 i),
-// CG groups at a time (16 for up to 8 rows, 8 for up to 16); the lane's
-// codes for 32 groups load into registers at once.  The buffer is small
-// enough for three blocks per CU, whose load and compute phases interleave.  Token slots past
-// the job's rows hold stale LDS contents: an MFMA output column depends on
-// its own B column only, and those columns are never stored.
+// one round of groups at a time (32 groups for up to 4 rows, 16 for up to 8,
+// 8 for up to 16); the lane's codes for 32 groups load into registers at
+// once.  The buffer is small enough for three blocks per CU, whose load and
+// compute phases interleave.  Token slots past the job's rows hold stale LDS
+// contents: an MFMA output column depends on its own B column only, and
+// those columns are never stored.
 typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
 
 constexpr int kCodeGroups = 32;                 // groups of codes held in registers
-// one round: 16 rows of 8 groups, or 8 rows of 16 groups
+// B area of one round: 16 rows of 8 groups, 8 rows of 16 or 4 rows of 32
 constexpr int kBufHalfs = 16 * (8 * kGroup + 8) > 8 * (16 * kGroup + 8) ? 16 * (8 * kGroup + 8)
                                                                        : 8 * (16 * kGroup + 8);
 struct TileBuf {
   __attribute__((aligned(16))) _Float16 bh[kBufHalfs];
   __attribute__((aligned(16))) _Float16 bl[kBufHalfs];
-  __attribute__((aligned(16))) uint32_t sb[16 * 64];   // [group][64 rows] (scale, bias) words
+  __attribute__((aligned(16))) uint32_t sb[32 * 64];   // [group][64 rows] (scale, bias) words
   float xs[8 * 16 * 2];                                // [token][group][part] B group sums
 };
 
@@ -409,9 +410,14 @@ struct TileSrc {
   const int *brow;        // LDS: B row of each token slot
 };
 
+// A buffer resource built from wave-uniform parts (readfirstlane), so that
+// the compiler keeps it in scalar registers wherever it is used.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0,
-                                           int(bytes < 0x7fffffffu ? bytes : 0x7fffffffu), 0x00020000);
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v)), hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(uint32_t(bytes < 0x7fffffffu ? bytes : 0x7fffffffu));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>((uint64_t(hi) << 32) | lo), (short)0, int(n),
+                                           0x00020000);
 }
 
 // 16 codes of a lane for one group: the same words load16 reads, by offset.
@@ -438,45 +444,59 @@ __device__ __forceinline__ void load_codes(const TileSrc &src, int row, int grp,
 }
 
 // LDS loads of groups [g0, g0 + gq) into `buf`; wave w takes every fourth.
-template <int CG>
-__device__ __forceinline__ void chunk_dma(const TileSrc &src, TileBuf &buf, int g0, int gq, int n_groups) {
+template <int CG, class Buf>
+__device__ __forceinline__ void chunk_dma(const TileSrc &src, Buf &buf, int g0, int gq, int n_groups) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int kRow = CG * kGroup + 8;            // B row stride in LDS (halfs)
   constexpr int kSegs = CG * kGroup / 512;         // 1 KB segments per B row
+  // the B row of token slot n is lane n's: read from LDS once, before any
+  // DMA load (an LDS read behind a DMA load in flight waits for it)
+  const int lane_brow = src.brow[min(lane, src.m - 1)];
   // B rows: one load per (token row, hi/lo, segment)
   for (int q = wave; q < 2 * kSegs * src.m; q += kWaves) {
     const int n = q / (2 * kSegs), hl = (q / kSegs) & 1, seg = q % kSegs;
     const int k0 = seg * 512 + lane * 8;
-    const _Float16 *row = (hl ? src.bl : src.bh) + size_t(src.brow[n]) * src.K + g0 * kGroup;
+    const int brow_n = __builtin_amdgcn_readlane(lane_brow, n);
+    const _Float16 *row = (hl ? src.bl : src.bh) + size_t(brow_n) * src.K + g0 * kGroup;
     _Float16 *dst = (hl ? buf.bl : buf.bh) + n * kRow + seg * 512;
     if (k0 < gq * kGroup)
       __builtin_amdgcn_global_load_lds((gvoid *)(row + k0), (lvoid *)dst, 16, 0, 0);
   }
   // (scale, bias) words: one load per group, lane = tile row
-  for (int Q = wave; Q < gq; Q += kWaves) {
-    const int row = src.r0 + lane, grp = g0 + Q;
-    const uint32_t *p = src.sb_group_major ? src.sb + size_t(grp) * src.sb_stride + row
-                                           : src.sb + size_t(row) * src.sb_stride + grp;
-    __builtin_amdgcn_global_load_lds((gvoid *)p, (lvoid *)(buf.sb + Q * 64), 4, 0, 0);
+#pragma unroll
+  for (int i = 0; i < (CG + kWaves - 1) / kWaves; ++i) {
+    const int Q = wave + kWaves * i;
+    if (Q < gq) {
+      const int row = src.r0 + lane, grp = g0 + Q;
+      const uint32_t *p = src.sb_group_major ? src.sb + size_t(grp) * src.sb_stride + row
+                                             : src.sb + size_t(row) * src.sb_stride + grp;
+      __builtin_amdgcn_global_load_lds((gvoid *)p, (lvoid *)(buf.sb + Q * 64), 4, 0, 0);
+    }
   }
-  // group sums: entry i = (token n, group Q, part h)
+  // group sums: entry i = (token n, group Q, part h); at most 16 x 16 x 2
+  // or 8 x 32 x 1 entries, 8 chunks of 64
   const int ents = src.m * CG * src.parts;
-  for (int q = wave; q * 64 < ents; q += kWaves) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int q = wave + kWaves * c;
     const int i = q * 64 + lane, n = i / (CG * src.parts), Q = (i / src.parts) % CG, h = i % src.parts;
-    if (i < ents && Q < gq) {
-      const float *p = src.xsum + (size_t(src.brow[n]) * n_groups + g0 + Q) * src.parts + h;
+    const int brow_n = __builtin_amdgcn_ds_bpermute(min(n, 63) << 2, lane_brow);
+    if (q * 64 < ents && i < ents && Q < gq) {
+      const float *p = src.xsum + (size_t(brow_n) * n_groups + g0 + Q) * src.parts + h;
       __builtin_amdgcn_global_load_lds((gvoid *)p, (lvoid *)(buf.xs + q * 64), 4, 0, 0);
     }
   }
 }
 
-template <int BITS, int CG>
-__device__ __forceinline__ void chunk_mma(const TileSrc &src, const TileBuf &buf, const uint32_t (&w)[kCodeGroups][3],
+template <int BITS, int CG, int ROWS, class Buf>
+__device__ __forceinline__ void chunk_mma(const TileSrc &src, const Buf &buf, const uint32_t (&w)[kCodeGroups][3],
                                           int q0, int gq, floatx4 &acc) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // token slot of the lane's B column; with 16-group rounds only 8 rows are
-  // staged, so slots 8..15 (past m) read rows 0..7 (their columns are unused)
-  const int g = lane >> 4, n = CG == 16 ? (lane & 7) : (lane & 15);
+  // token slot of the lane's B column; when a round stages fewer than 16
+  // rows, slots past them (past m) read the staged rows again (their
+  // columns are unused)
+  static_assert(ROWS == 4 || ROWS == 8 || ROWS == 16, "rounds stage 4, 8 or 16 token rows");
+  const int g = lane >> 4, n = lane & (ROWS - 1);
   constexpr int kRow = CG * kGroup + 8;
 #pragma unroll
   for (int Q = 0; Q < CG; ++Q) {
@@ -502,36 +522,78 @@ __device__ __forceinline__ void chunk_mma(const TileSrc &src, const TileBuf &buf
   }
 }
 
-template <int BITS, int CG>
+// s_waitcnt on the vector-memory count only: at most N loads of this wave
+// still in flight (the expcnt and lgkmcnt fields at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_sched_barrier(0);   // no use of a pending load is scheduled above the wait
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// A workgroup barrier with no memory fence: this wave's LDS operations have
+// completed (lgkmcnt 0) and the empty asm statements keep the compiler from
+// moving memory operations across it, but global loads in flight stay in
+// flight (a fenced barrier waits for all of them).  LDS written by DMA loads
+// is covered only by the waits the caller does before it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// The rounds of a work item, with an early start: round 0's operands go to
+// LDS first, then every code of the batch loads in group order, and round 0
+// waits only for its operands (the codes are the loads issued after them,
+// and the counter retires loads in issue order); its groups then consume
+// the codes as they land.  Later rounds load their operands after the
+// previous round is computed.  Rounds: 32 groups of 4 rows, 16 of 8 or 8
+// of 16.
+template <int BITS, int CG, int ROWS>
 __device__ __forceinline__ void mfma_tile(const TileSrc &src, TileBuf &buf, floatx4 &acc) {
+  static_assert(ROWS * (CG * kGroup + 8) <= kBufHalfs, "round does not fit the B area");
+  static_assert(CG <= 32 && ROWS * CG * 2 <= 8 * 16 * 2, "round does not fit the (scale, bias) or sum areas");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int arow = src.r0 + wave * 16 + (lane & 15), g = lane >> 4;
   const int n_groups = src.K / kGroup;
+  constexpr int kCodeLoads = (BITS == 3 ? 2 : 1) * kCodeGroups;   // load_codes' vector loads
   acc = floatx4{0, 0, 0, 0};
   for (int g0 = 0; g0 < n_groups; g0 += kCodeGroups) {
+    const int nr = (min(kCodeGroups, n_groups - g0) + CG - 1) / CG;
+    chunk_dma<CG>(src, buf, g0, min(CG, n_groups - g0), n_groups);
+    asm volatile("" ::: "memory");   // the codes are issued after round 0's operands
     uint32_t w[kCodeGroups][3];
 #pragma unroll
     for (int Q = 0; Q < kCodeGroups; ++Q) load_codes<BITS>(src, arow, min(g0 + Q, n_groups - 1), g, w[Q]);
+    asm volatile("" ::: "memory");   // ... and all of them before the wait
+    wait_vm<(kCodeLoads < 63 ? kCodeLoads : 63)>();
+    lds_barrier();
 #pragma unroll
     for (int cs = 0; cs < kCodeGroups / CG; ++cs) {
       const int cb = g0 + cs * CG;
-      if (cb < n_groups) {
-        const int gq = min(CG, n_groups - cb);
-        __syncthreads();                 // the buffer's previous reads are done
-        chunk_dma<CG>(src, buf, cb, gq, n_groups);
-        __builtin_amdgcn_s_waitcnt(0);   // this round's LDS loads and the codes have landed
-        __syncthreads();                 // ... for every wave
-        chunk_mma<BITS, CG>(src, buf, w, cs * CG, gq, acc);
+      if (cs < nr) {
+        if (cs > 0) {
+          lds_barrier();   // every wave is done with round cs - 1
+          chunk_dma<CG>(src, buf, cb, min(CG, n_groups - cb), n_groups);
+          wait_vm<0>();
+          lds_barrier();
+        }
+        chunk_mma<BITS, CG, ROWS>(src, buf, w, cs * CG, min(CG, n_groups - cb), acc);
       }
     }
+    __syncthreads();   // the buffer is free for the next batch or work item
   }
-  __syncthreads();   // the buffer is free for the next work item
 }
 
 template <int BITS>
 __device__ __forceinline__ void mfma_tile_any(const TileSrc &src, TileBuf &buf, floatx4 &acc) {
-  if (src.m > 8) mfma_tile<BITS, 8>(src, buf, acc);   // (rounds of 16 groups hold 8 rows)
-  else mfma_tile<BITS, 16>(src, buf, acc);
+  if (src.m > 8) mfma_tile<BITS, 8, 16>(src, buf, acc);
+  else if (src.m > 4) mfma_tile<BITS, 16, 8>(src, buf, acc);
+  else mfma_tile<BITS, 32, 4>(src, buf, acc);
 }
 
 __device__ __forceinline__ void set_brows(const PrefillArgs &a, const Job &j, int *brow, bool act_rows) {
