@@ -167,6 +167,7 @@ __global__ __launch_bounds__(128) void pf_topk_kernel(PrefillArgs a, const doubl
                                                       int32_t *expert_ptr, int32_t *entry_row,
                                                       int32_t *entry_rank) {
   __shared__ double lg[kMaxExperts];
+  __shared__ uint32_t k32[kMaxExperts];
   __shared__ int sel[kMaxTopK];
   __shared__ double selv[kMaxTopK];
   __shared__ uint32_t prev;
@@ -178,24 +179,36 @@ __global__ __launch_bounds__(128) void pf_topk_kernel(PrefillArgs a, const doubl
   const int E = a.n_experts, k = a.top_k, t = a.t;
   const int r = blockIdx.x;
   const int Ep = (E + 7) & ~7;
-  for (int e = threadIdx.x; e < Ep; e += 128) lg[e] = e < E ? logits[size_t(r) * E + e] : -__builtin_inf();
+  // logits (+ 0.0 folds -0 into +0, so equal values tie on the id alone) and
+  // 32-bit order keys of them rounded to float32; padding keys are 0, below
+  // every logit's key
+  for (int e = threadIdx.x; e < Ep; e += 128) {
+    const double v = e < E ? logits[size_t(r) * E + e] + 0.0 : -__builtin_inf();
+    lg[e] = v;
+    k32[e] = e < E ? order_key32(float(v)) : 0u;
+  }
   if (threadIdx.x < kMaxTopK) sel[threadIdx.x] = 0;
   __syncthreads();
+  // rank = entries ahead in (logit descending, id ascending).  Rounding to
+  // float32 never reverses an order, so a larger key is a larger logit and
+  // a smaller key a smaller one; only entries whose keys are equal are
+  // compared again in float64, and only for an entry that can still place
   for (int e = threadIdx.x; e < E; e += 128) {
-    const double v = lg[e];
-    const double2 *row = reinterpret_cast<const double2 *>(lg);
-    int rank = 0;
-    for (int f2 = 0; f2 < Ep / 2; f2 += 4) {
-      const double2 o0 = row[f2], o1 = row[f2 + 1], o2 = row[f2 + 2], o3 = row[f2 + 3];
-      const int f = 2 * f2;
-      rank += int(o0.x > v) + int(o0.y > v) + int(o1.x > v) + int(o1.y > v) +
-              int(o2.x > v) + int(o2.y > v) + int(o3.x > v) + int(o3.y > v);
-      rank += (int(o0.x == v) & int(f < e)) + (int(o0.y == v) & int(f + 1 < e)) +
-              (int(o1.x == v) & int(f + 2 < e)) + (int(o1.y == v) & int(f + 3 < e)) +
-              (int(o2.x == v) & int(f + 4 < e)) + (int(o2.y == v) & int(f + 5 < e)) +
-              (int(o3.x == v) & int(f + 6 < e)) + (int(o3.y == v) & int(f + 7 < e));
+    const uint32_t ke = k32[e];
+    const uint4 *kr = reinterpret_cast<const uint4 *>(k32);
+    int gt = 0, eq = 0;
+    for (int f4 = 0; f4 < Ep / 4; ++f4) {
+      const uint4 o = kr[f4];
+      gt += int(o.x > ke) + int(o.y > ke) + int(o.z > ke) + int(o.w > ke);
+      eq += int(o.x == ke) + int(o.y == ke) + int(o.z == ke) + int(o.w == ke);
     }
-    if (rank < k) { sel[rank] = e; selv[rank] = v; }
+    int rank = gt;
+    if (gt < k && eq > 1) {   // float32 ties (the entry itself is one of them)
+      const double v = lg[e];
+      for (int f = 0; f < E; ++f)
+        if (k32[f] == ke) rank += int(lg[f] > v) + (int(lg[f] == v) & int(f < e));
+    }
+    if (rank < k) { sel[rank] = e; selv[rank] = lg[e]; }
   }
   __syncthreads();
   if (wave == 0) {
