@@ -398,12 +398,15 @@ constexpr int kCodeGroups = 32;                 // groups of codes held in regis
 // B area of one round: 16 rows of 8 groups, 8 rows of 16 or 4 rows of 32
 constexpr int kBufHalfs = 16 * (8 * kGroup + 8) > 8 * (16 * kGroup + 8) ? 16 * (8 * kGroup + 8)
                                                                        : 8 * (16 * kGroup + 8);
-struct TileBuf {
+template <int SBG>   // rounds of up to SBG groups
+struct TileBufT {
   __attribute__((aligned(16))) _Float16 bh[kBufHalfs];
   __attribute__((aligned(16))) _Float16 bl[kBufHalfs];
-  __attribute__((aligned(16))) uint32_t sb[32 * 64];   // [group][64 rows] (scale, bias) words
-  float xs[8 * 16 * 2];                                // [token][group][part] B group sums
+  __attribute__((aligned(16))) uint32_t sb[SBG * 64];   // [group][64 rows] (scale, bias) words
+  float xs[8 * 16 * 2];                                 // [token][group][part] B group sums
 };
+typedef TileBufT<32> TileBuf;   // gate/up: rounds of up to 32 groups
+typedef TileBufT<8> DownBuf;    // down: rounds of 8 groups (four blocks per CU)
 
 // Where a work item's operands live.
 struct TileSrc {
@@ -501,8 +504,8 @@ __device__ __forceinline__ void chunk_dma(const TileSrc &src, Buf &buf, int g0, 
   }
 }
 
-template <int BITS, int CG, int ROWS, class Buf>
-__device__ __forceinline__ void chunk_mma(const TileSrc &src, const Buf &buf, const uint32_t (&w)[kCodeGroups][3],
+template <int BITS, int CG, int ROWS, int KCG, class Buf>
+__device__ __forceinline__ void chunk_mma(const TileSrc &src, const Buf &buf, const uint32_t (&w)[KCG][3],
                                           int q0, int gq, floatx4 &acc) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // token slot of the lane's B column; when a round stages fewer than 16
@@ -566,27 +569,27 @@ __device__ __forceinline__ void lds_barrier() {
 // the codes as they land.  Later rounds load their operands after the
 // previous round is computed.  Rounds: 32 groups of 4 rows, 16 of 8 or 8
 // of 16.
-template <int BITS, int CG, int ROWS>
-__device__ __forceinline__ void mfma_tile(const TileSrc &src, TileBuf &buf, floatx4 &acc) {
+template <int BITS, int CG, int ROWS, int KCG, int SBG>
+__device__ __forceinline__ void mfma_tile(const TileSrc &src, TileBufT<SBG> &buf, floatx4 &acc) {
   static_assert(ROWS * (CG * kGroup + 8) <= kBufHalfs, "round does not fit the B area");
-  static_assert(CG <= 32 && ROWS * CG * 2 <= 8 * 16 * 2, "round does not fit the (scale, bias) or sum areas");
+  static_assert(CG <= SBG && CG <= KCG && ROWS * CG * 2 <= 8 * 16 * 2, "round does not fit the (scale, bias) or sum areas");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int arow = src.r0 + wave * 16 + (lane & 15), g = lane >> 4;
   const int n_groups = src.K / kGroup;
-  constexpr int kCodeLoads = (BITS == 3 ? 2 : 1) * kCodeGroups;   // load_codes' vector loads
+  constexpr int kCodeLoads = (BITS == 3 ? 2 : 1) * KCG;   // load_codes' vector loads
   acc = floatx4{0, 0, 0, 0};
-  for (int g0 = 0; g0 < n_groups; g0 += kCodeGroups) {
-    const int nr = (min(kCodeGroups, n_groups - g0) + CG - 1) / CG;
+  for (int g0 = 0; g0 < n_groups; g0 += KCG) {
+    const int nr = (min(KCG, n_groups - g0) + CG - 1) / CG;
     chunk_dma<CG>(src, buf, g0, min(CG, n_groups - g0), n_groups);
     asm volatile("" ::: "memory");   // the codes are issued after round 0's operands
-    uint32_t w[kCodeGroups][3];
+    uint32_t w[KCG][3];
 #pragma unroll
-    for (int Q = 0; Q < kCodeGroups; ++Q) load_codes<BITS>(src, arow, min(g0 + Q, n_groups - 1), g, w[Q]);
+    for (int Q = 0; Q < KCG; ++Q) load_codes<BITS>(src, arow, min(g0 + Q, n_groups - 1), g, w[Q]);
     asm volatile("" ::: "memory");   // ... and all of them before the wait
     wait_vm<(kCodeLoads < 63 ? kCodeLoads : 63)>();
     lds_barrier();
 #pragma unroll
-    for (int cs = 0; cs < kCodeGroups / CG; ++cs) {
+    for (int cs = 0; cs < KCG / CG; ++cs) {
       const int cb = g0 + cs * CG;
       if (cs < nr) {
         if (cs > 0) {
@@ -595,7 +598,7 @@ __device__ __forceinline__ void mfma_tile(const TileSrc &src, TileBuf &buf, floa
           wait_vm<0>();
           lds_barrier();
         }
-        chunk_mma<BITS, CG, ROWS>(src, buf, w, cs * CG, min(CG, n_groups - cb), acc);
+        chunk_mma<BITS, CG, ROWS, KCG>(src, buf, w, cs * CG, min(CG, n_groups - cb), acc);
       }
     }
     __syncthreads();   // the buffer is free for the next batch or work item
@@ -604,9 +607,17 @@ __device__ __forceinline__ void mfma_tile(const TileSrc &src, TileBuf &buf, floa
 
 template <int BITS>
 __device__ __forceinline__ void mfma_tile_any(const TileSrc &src, TileBuf &buf, floatx4 &acc) {
-  if (src.m > 8) mfma_tile<BITS, 8, 16>(src, buf, acc);
-  else if (src.m > 4) mfma_tile<BITS, 16, 8>(src, buf, acc);
-  else mfma_tile<BITS, 32, 4>(src, buf, acc);
+  if (src.m > 8) mfma_tile<BITS, 8, 16, kCodeGroups>(src, buf, acc);
+  else if (src.m > 4) mfma_tile<BITS, 16, 8, kCodeGroups>(src, buf, acc);
+  else mfma_tile<BITS, 32, 4, kCodeGroups>(src, buf, acc);
+}
+
+// down: 8 groups of codes in registers and rounds of 8 groups for any m
+// (K = I is 8 groups at I = 512: one round, and a register budget and LDS
+// area small enough for four blocks per CU)
+template <int BITS>
+__device__ __forceinline__ void mfma_tile_down(const TileSrc &src, DownBuf &buf, floatx4 &acc) {
+  mfma_tile<BITS, 8, 16, 8>(src, buf, acc);
 }
 
 __device__ __forceinline__ void set_brows(const PrefillArgs &a, const Job &j, int *brow, bool act_rows) {
@@ -698,7 +709,7 @@ __global__ __launch_bounds__(kThreads) void pf_gate_up_kernel(PrefillArgs a) {
 // down: work item (job, 64 output rows); writes the routing-weighted rows of
 // every (row, rank) entry of the job.
 __global__ __launch_bounds__(kThreads) void pf_down_kernel(PrefillArgs a) {
-  __shared__ TileBuf buf;
+  __shared__ DownBuf buf;
   __shared__ int brow[16];
   const int H = a.hidden, I = a.inter;
   const int tiles = H / 64;
@@ -733,9 +744,9 @@ __global__ __launch_bounds__(kThreads) void pf_down_kernel(PrefillArgs a) {
       src.m = j.m;
       src.brow = brow;
       switch (bits) {
-        case 4: mfma_tile_any<4>(src, buf, acc); break;
-        case 3: mfma_tile_any<3>(src, buf, acc); break;
-        default: mfma_tile_any<2>(src, buf, acc); break;
+        case 4: mfma_tile_down<4>(src, buf, acc); break;
+        case 3: mfma_tile_down<3>(src, buf, acc); break;
+        default: mfma_tile_down<2>(src, buf, acc); break;
       }
     } else if (threadIdx.x == 0) {
       __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
