@@ -12,7 +12,8 @@
 //   P1 router logits (float64) of the t rows and, for the experts, an f16
 //      hi/lo split of x plus per-64 group sums of x;
 //   P2 per-row top-k and weights; the last block groups the rows by expert
-//      (experts ascending, rows ascending) and lists the experts in use;
+//      (experts ascending, rows ascending) and lists the sub-jobs (at most
+//      16 rows of one expert), longest first;
 //   P3 gate/up: per (used expert, 64 gate/up rows), MFMA 16x16x32 f16 tiles
 //      of 16 rows x 16 tokens (1 or 2 token tiles for m <= 16 or <= 32);
 //   P4 down: per (used expert, 64 output rows), same tiles, writes the
@@ -232,14 +233,15 @@ __global__ __launch_bounds__(128) void pf_topk_kernel(PrefillArgs a, const doubl
   __syncthreads();
   for (int p = threadIdx.x; p < t * k; p += 128) atomicOr(&emask[all_sel[p]], 1u << (p / k));
   __syncthreads();
-  // exclusive scan over experts of (rows << 20 | big << 10 | used), two
-  // experts a thread: `used` numbers the experts in use, `big` those with
-  // more than 16 rows (they run as two sub-jobs of at most 16 rows)
+  // exclusive scan over experts of (rows << 20 | heavy << 10 | light), two
+  // experts a thread: an expert with more than 8 rows is heavy (one
+  // sub-job, two above 16 rows: sub-jobs hold at most 16 rows), one with 1-8
+  // rows light
   {
     const int e0 = 2 * threadIdx.x, e1 = e0 + 1;
     const int c0 = e0 < E ? __popc(emask[e0]) : 0, c1 = e1 < E ? __popc(emask[e1]) : 0;
-    const int v0 = (c0 << 20) | (int(c0 > 16) << 10) | int(c0 > 0);
-    const int v1 = (c1 << 20) | (int(c1 > 16) << 10) | int(c1 > 0);
+    const int v0 = (c0 << 20) | ((c0 > 8 ? 1 + int(c0 > 16) : 0) << 10) | int(c0 > 0 && c0 <= 8);
+    const int v1 = (c1 << 20) | ((c1 > 8 ? 1 + int(c1 > 16) : 0) << 10) | int(c1 > 0 && c1 <= 8);
     int incl = v0 + v1;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -254,29 +256,32 @@ __global__ __launch_bounds__(128) void pf_topk_kernel(PrefillArgs a, const doubl
     if (threadIdx.x == 0) cnt[E] = wsum[0] + wsum[1];
   }
   __syncthreads();
-  // sub-jobs (expert, first row): experts ascending, then the shared expert
+  // sub-jobs (expert, first row), longest first: the shared expert's, then
+  // the heavy experts', then the light ones' (experts ascending in each), so
+  // that the items with the most rounds start their loads first
+  const int n_shared = t > 16 ? 2 : 1, n_heavy = (cnt[E] >> 10) & 1023;
   for (int e = threadIdx.x; e <= E; e += 128) {
     const int v = cnt[e];
     expert_ptr[e] = v >> 20;
     if (e < E && emask[e]) {
-      const int sj = ((v >> 10) & 1023) + (v & 1023);
+      const int c = __popc(emask[e]);
+      const int sj = c > 8 ? n_shared + ((v >> 10) & 1023) : n_shared + n_heavy + (v & 1023);
       a.meta[1 + 2 * sj] = e;
       a.meta[2 + 2 * sj] = 0;
-      if (__popc(emask[e]) > 16) {
+      if (c > 16) {
         a.meta[3 + 2 * sj] = e;
         a.meta[4 + 2 * sj] = 16;
       }
     }
   }
   if (threadIdx.x == 0) {
-    const int v = cnt[E], n_sub = ((v >> 10) & 1023) + (v & 1023);
-    a.meta[1 + 2 * n_sub] = -1;
-    a.meta[2 + 2 * n_sub] = 0;
+    a.meta[1] = -1;
+    a.meta[2] = 0;
     if (t > 16) {
-      a.meta[3 + 2 * n_sub] = -1;
-      a.meta[4 + 2 * n_sub] = 16;
+      a.meta[3] = -1;
+      a.meta[4] = 16;
     }
-    a.meta[0] = n_sub + (t > 16 ? 2 : 1);
+    a.meta[0] = n_shared + n_heavy + (cnt[E] & 1023);
   }
   for (int p = threadIdx.x; p < t * k; p += 128) {
     const int e = all_sel[p], r = p / k;
