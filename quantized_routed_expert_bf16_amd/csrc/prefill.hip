@@ -464,6 +464,20 @@ __device__ __forceinline__ void load_codes(const TileSrc &src, int row, int grp,
   }
 }
 
+// 4-bit row-major codes, two groups a load: lane (row, slot g) reads bytes
+// 16 g .. 16 g + 15 of the 64 bytes of groups grp and grp + 1 (slots 0, 1:
+// halves of grp, slots 2, 3: of grp + 1) into w0 (lower 8 bytes) and w1
+// (upper 8).  Reads past a row's last group (an odd group count) stay inside
+// the code section or are dropped by the resource's bound, and are never
+// used.
+__device__ __forceinline__ void load_codes_pair(const TileSrc &src, int row, int grp, int g, uint32_t (&w0)[3],
+                                                uint32_t (&w1)[3]) {
+  const uint32_t off = uint32_t(row) * src.row_bytes + uint32_t(grp) * (kGroup / 2) + 16 * g;
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(src.codes, off, 0, 0);
+  w0[0] = v[0]; w0[1] = v[1]; w0[2] = 0;
+  w1[0] = v[2]; w1[1] = v[3]; w1[2] = 0;
+}
+
 // LDS loads of groups [g0, g0 + gq) into `buf`; wave w takes every fourth.
 template <int CG, class Buf>
 __device__ __forceinline__ void chunk_dma(const TileSrc &src, Buf &buf, int g0, int gq, int n_groups) {
@@ -509,10 +523,19 @@ __device__ __forceinline__ void chunk_dma(const TileSrc &src, Buf &buf, int g0, 
   }
 }
 
-template <int BITS, int CG, int ROWS, int KCG, class Buf>
+// PAIR: the codes were loaded two groups a load (load_codes_pair).  One
+// exchange of the upper two words with slot g ^ 2 (lane ^ 32) leaves every
+// slot 16 codes of each group of the pair: slot g holds codes kb .. kb + 15
+// of group Q with kb = 16 (2 (g & 1) + ((g >> 1) ^ (Q & 1))), its own lower
+// words when (g >> 1) == (Q & 1) and the received ones otherwise; the B
+// fragments are read at the same kb.
+template <int BITS, int CG, int ROWS, int KCG, bool PAIR, class Buf>
 __device__ __forceinline__ void chunk_mma(const TileSrc &src, const Buf &buf, const uint32_t (&w)[KCG][3],
                                           int q0, int gq, floatx4 &acc) {
+  static_assert(!PAIR || (BITS == 4 && CG % 2 == 0), "paired loads: 4-bit codes, whole pairs a round");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int partner = (lane ^ 32) * 4;   // ds_bpermute address of slot g ^ 2
+  uint32_t ex0 = 0, ex1 = 0;
   // token slot of the lane's B column; when a round stages fewer than 16
   // rows, slots past them (past m) read the staged rows again (their
   // columns are unused)
@@ -523,13 +546,25 @@ __device__ __forceinline__ void chunk_mma(const TileSrc &src, const Buf &buf, co
   for (int Q = 0; Q < CG; ++Q) {
     if (Q < gq) {
       half8 A[2];
-      codes_to_a<BITS>(w[q0 + Q], A, g & 1);
+      int kb = 16 * g;   // first of the lane's 16 codes of group Q
+      if constexpr (PAIR) {
+        if ((Q & 1) == 0) {   // one exchange serves both groups of the pair
+          ex0 = __builtin_amdgcn_ds_bpermute(partner, w[q0 + Q + 1][0]);
+          ex1 = __builtin_amdgcn_ds_bpermute(partner, w[q0 + Q + 1][1]);
+        }
+        const bool own = (g >> 1) == (Q & 1);
+        const uint32_t aw[3] = {own ? w[q0 + (Q & ~1)][0] : ex0, own ? w[q0 + (Q & ~1)][1] : ex1, 0u};
+        codes_to_a<BITS>(aw, A, 0);
+        kb = 16 * (2 * (g & 1) + ((g >> 1) ^ (Q & 1)));
+      } else {
+        codes_to_a<BITS>(w[q0 + Q], A, g & 1);
+      }
       const uint4 sq = *static_cast<const uint4 *>(__builtin_assume_aligned(buf.sb + Q * 64 + wave * 16 + 4 * g, 16));
       const uint32_t sw4[4] = {sq.x, sq.y, sq.z, sq.w};
       floatx4 cgv = {0, 0, 0, 0};
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const int at = n * kRow + Q * kGroup + 16 * g + 8 * st;
+        const int at = n * kRow + Q * kGroup + kb + 8 * st;
         const half8 Bh = *static_cast<const half8 *>(__builtin_assume_aligned(buf.bh + at, 16));
         const half8 Bl = *static_cast<const half8 *>(__builtin_assume_aligned(buf.bl + at, 16));
         cgv = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[st], Bh, cgv, 0, 0, 0);
@@ -574,22 +609,28 @@ __device__ __forceinline__ void lds_barrier() {
 // the codes as they land.  Later rounds load their operands after the
 // previous round is computed.  Rounds: 32 groups of 4 rows, 16 of 8 or 8
 // of 16.
-template <int BITS, int CG, int ROWS, int KCG, int SBG>
+template <int BITS, int CG, int ROWS, int KCG, bool PAIR, int SBG>
 __device__ __forceinline__ void mfma_tile(const TileSrc &src, TileBufT<SBG> &buf, floatx4 &acc) {
   static_assert(ROWS * (CG * kGroup + 8) <= kBufHalfs, "round does not fit the B area");
   static_assert(CG <= SBG && CG <= KCG && ROWS * CG * 2 <= 8 * 16 * 2, "round does not fit the (scale, bias) or sum areas");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int arow = src.r0 + wave * 16 + (lane & 15), g = lane >> 4;
   const int n_groups = src.K / kGroup;
-  constexpr int kCodeLoads = (BITS == 3 ? 2 : 1) * KCG;   // load_codes' vector loads
+  constexpr int kCodeLoads = PAIR ? KCG / 2 : (BITS == 3 ? 2 : 1) * KCG;   // the code loads' count
   acc = floatx4{0, 0, 0, 0};
   for (int g0 = 0; g0 < n_groups; g0 += KCG) {
     const int nr = (min(KCG, n_groups - g0) + CG - 1) / CG;
     chunk_dma<CG>(src, buf, g0, min(CG, n_groups - g0), n_groups);
     asm volatile("" ::: "memory");   // the codes are issued after round 0's operands
     uint32_t w[KCG][3];
+    if constexpr (PAIR) {
 #pragma unroll
-    for (int Q = 0; Q < KCG; ++Q) load_codes<BITS>(src, arow, min(g0 + Q, n_groups - 1), g, w[Q]);
+      for (int P = 0; P < KCG / 2; ++P)
+        load_codes_pair(src, arow, min(g0 + 2 * P, (n_groups - 1) & ~1), g, w[2 * P], w[2 * P + 1]);
+    } else {
+#pragma unroll
+      for (int Q = 0; Q < KCG; ++Q) load_codes<BITS>(src, arow, min(g0 + Q, n_groups - 1), g, w[Q]);
+    }
     asm volatile("" ::: "memory");   // ... and all of them before the wait
     wait_vm<(kCodeLoads < 63 ? kCodeLoads : 63)>();
     lds_barrier();
@@ -603,7 +644,7 @@ __device__ __forceinline__ void mfma_tile(const TileSrc &src, TileBufT<SBG> &buf
           wait_vm<0>();
           lds_barrier();
         }
-        chunk_mma<BITS, CG, ROWS, KCG>(src, buf, w, cs * CG, min(CG, n_groups - cb), acc);
+        chunk_mma<BITS, CG, ROWS, KCG, PAIR>(src, buf, w, cs * CG, min(CG, n_groups - cb), acc);
       }
     }
     __syncthreads();   // the buffer is free for the next batch or work item
@@ -612,9 +653,10 @@ __device__ __forceinline__ void mfma_tile(const TileSrc &src, TileBufT<SBG> &buf
 
 template <int BITS>
 __device__ __forceinline__ void mfma_tile_any(const TileSrc &src, TileBuf &buf, floatx4 &acc) {
-  if (src.m > 8) mfma_tile<BITS, 8, 16, kCodeGroups>(src, buf, acc);
-  else if (src.m > 4) mfma_tile<BITS, 16, 8, kCodeGroups>(src, buf, acc);
-  else mfma_tile<BITS, 32, 4, kCodeGroups>(src, buf, acc);
+  // (4-bit records are row-major: their codes load two groups a load)
+  if (src.m > 8) mfma_tile<BITS, 8, 16, kCodeGroups, BITS == 4>(src, buf, acc);
+  else if (src.m > 4) mfma_tile<BITS, 16, 8, kCodeGroups, BITS == 4>(src, buf, acc);
+  else mfma_tile<BITS, 32, 4, kCodeGroups, BITS == 4>(src, buf, acc);
 }
 
 // down: 8 groups of codes in registers and rounds of 8 groups for any m
@@ -622,7 +664,7 @@ __device__ __forceinline__ void mfma_tile_any(const TileSrc &src, TileBuf &buf, 
 // area small enough for four blocks per CU)
 template <int BITS>
 __device__ __forceinline__ void mfma_tile_down(const TileSrc &src, DownBuf &buf, floatx4 &acc) {
-  mfma_tile<BITS, 8, 16, 8>(src, buf, acc);
+  mfma_tile<BITS, 8, 16, 8, false>(src, buf, acc);
 }
 
 __device__ __forceinline__ void set_brows(const PrefillArgs &a, const Job &j, int *brow, bool act_rows) {
@@ -635,7 +677,7 @@ __device__ __forceinline__ void set_brows(const PrefillArgs &a, const Job &j, in
 // of the tile's 32 columns, stored as f16 hi/lo halves in the MFMA order of
 // the job's record, plus the sum of the 32 values for the down pass's bias
 // term.
-__global__ __launch_bounds__(kThreads) void pf_gate_up_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads, 3) void pf_gate_up_kernel(PrefillArgs a) {
   __shared__ TileBuf buf;
   __shared__ int brow[16];
   __shared__ float red[kWaves][16];
