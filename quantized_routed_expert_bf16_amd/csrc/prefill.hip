@@ -420,6 +420,7 @@ struct TileSrc {
   int row_bytes;          // bytes per packed row (row-major layout)
   int rows_total;         // rows of the matrix (group-major layout)
   const uint32_t *sb;     // (scale, bias) words
+  __amdgpu_buffer_rsrc_t sbr;   // the same words as a bounded resource (row-major records)
   bool sb_group_major;    // [group][rows] (else [row][groups])
   int sb_stride;          // groups per row, or rows per group
   const _Float16 *bh, *bl;   // B rows (row stride = K halfs)
@@ -479,7 +480,7 @@ __device__ __forceinline__ void load_codes_pair(const TileSrc &src, int row, int
 }
 
 // LDS loads of groups [g0, g0 + gq) into `buf`; wave w takes every fourth.
-template <int CG, class Buf>
+template <int CG, bool SBDMA, class Buf>
 __device__ __forceinline__ void chunk_dma(const TileSrc &src, Buf &buf, int g0, int gq, int n_groups) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int kRow = CG * kGroup + 8;            // B row stride in LDS (halfs)
@@ -497,9 +498,10 @@ __device__ __forceinline__ void chunk_dma(const TileSrc &src, Buf &buf, int g0, 
     if (k0 < gq * kGroup)
       __builtin_amdgcn_global_load_lds((gvoid *)(row + k0), (lvoid *)dst, 16, 0, 0);
   }
-  // (scale, bias) words: one load per group, lane = tile row
+  // (scale, bias) words of group-major records: one load per group, lane =
+  // tile row (row-major records load theirs through registers: sb_fetch)
 #pragma unroll
-  for (int i = 0; i < (CG + kWaves - 1) / kWaves; ++i) {
+  for (int i = 0; i < (SBDMA ? (CG + kWaves - 1) / kWaves : 0); ++i) {
     const int Q = wave + kWaves * i;
     if (Q < gq) {
       const int row = src.r0 + lane, grp = g0 + Q;
@@ -521,6 +523,43 @@ __device__ __forceinline__ void chunk_dma(const TileSrc &src, Buf &buf, int g0, 
       __builtin_amdgcn_global_load_lds((gvoid *)p, (lvoid *)(buf.xs + q * 64), 4, 0, 0);
     }
   }
+}
+
+// (scale, bias) words of a round from a row-major record ([row][groups]):
+// thread t takes tile row t / 4 and the quarter t % 4 of the round's CG
+// groups, a run of CG / 4 contiguous words, so that a wave's loads cover
+// whole rows (a load per group with lane = row touches 64 rows); the words
+// go to LDS group-major, [group][64 rows], once the round has landed.  Runs
+// past the section's end read 0 through the bounded resource, and groups
+// past the round's are never read.
+template <int CG>
+struct SbRun {
+  uint32_t v[CG / 4];
+};
+
+template <int CG>
+__device__ __forceinline__ void sb_fetch(const TileSrc &src, int g0, SbRun<CG> &r) {
+  static_assert(CG == 8 || CG == 16 || CG == 32, "runs of 2, 4 or 8 words");
+  const int t = threadIdx.x;
+  const uint32_t off = (uint32_t(src.r0 + t / 4) * src.sb_stride + g0 + (t % 4) * (CG / 4)) * 4;
+#pragma unroll
+  for (int h = 0; h < (CG / 4 + 3) / 4; ++h) {
+    if constexpr (CG == 8) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(src.sbr, off, 0, 0);
+      r.v[0] = v[0]; r.v[1] = v[1];
+    } else {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(src.sbr, off + 16 * h, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r.v[4 * h + j] = v[j];
+    }
+  }
+}
+
+template <int CG, class Buf>
+__device__ __forceinline__ void sb_store(Buf &buf, const SbRun<CG> &r) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < CG / 4; ++j) buf.sb[((t % 4) * (CG / 4) + j) * 64 + t / 4] = r.v[j];
 }
 
 // PAIR: the codes were loaded two groups a load (load_codes_pair).  One
@@ -609,7 +648,7 @@ __device__ __forceinline__ void lds_barrier() {
 // the codes as they land.  Later rounds load their operands after the
 // previous round is computed.  Rounds: 32 groups of 4 rows, 16 of 8 or 8
 // of 16.
-template <int BITS, int CG, int ROWS, int KCG, bool PAIR, int SBG>
+template <int BITS, int CG, int ROWS, int KCG, bool PAIR, bool SBROWS, int SBG>
 __device__ __forceinline__ void mfma_tile(const TileSrc &src, TileBufT<SBG> &buf, floatx4 &acc) {
   static_assert(ROWS * (CG * kGroup + 8) <= kBufHalfs, "round does not fit the B area");
   static_assert(CG <= SBG && CG <= KCG && ROWS * CG * 2 <= 8 * 16 * 2, "round does not fit the (scale, bias) or sum areas");
@@ -620,7 +659,9 @@ __device__ __forceinline__ void mfma_tile(const TileSrc &src, TileBufT<SBG> &buf
   acc = floatx4{0, 0, 0, 0};
   for (int g0 = 0; g0 < n_groups; g0 += KCG) {
     const int nr = (min(KCG, n_groups - g0) + CG - 1) / CG;
-    chunk_dma<CG>(src, buf, g0, min(CG, n_groups - g0), n_groups);
+    chunk_dma<CG, !SBROWS>(src, buf, g0, min(CG, n_groups - g0), n_groups);
+    SbRun<CG> sbw;
+    if constexpr (SBROWS) sb_fetch<CG>(src, g0, sbw);
     asm volatile("" ::: "memory");   // the codes are issued after round 0's operands
     uint32_t w[KCG][3];
     if constexpr (PAIR) {
@@ -633,6 +674,7 @@ __device__ __forceinline__ void mfma_tile(const TileSrc &src, TileBufT<SBG> &buf
     }
     asm volatile("" ::: "memory");   // ... and all of them before the wait
     wait_vm<(kCodeLoads < 63 ? kCodeLoads : 63)>();
+    if constexpr (SBROWS) sb_store<CG>(buf, sbw);
     lds_barrier();
 #pragma unroll
     for (int cs = 0; cs < KCG / CG; ++cs) {
@@ -640,8 +682,10 @@ __device__ __forceinline__ void mfma_tile(const TileSrc &src, TileBufT<SBG> &buf
       if (cs < nr) {
         if (cs > 0) {
           lds_barrier();   // every wave is done with round cs - 1
-          chunk_dma<CG>(src, buf, cb, min(CG, n_groups - cb), n_groups);
+          chunk_dma<CG, !SBROWS>(src, buf, cb, min(CG, n_groups - cb), n_groups);
+          if constexpr (SBROWS) sb_fetch<CG>(src, cb, sbw);
           wait_vm<0>();
+          if constexpr (SBROWS) sb_store<CG>(buf, sbw);
           lds_barrier();
         }
         chunk_mma<BITS, CG, ROWS, KCG, PAIR>(src, buf, w, cs * CG, min(CG, n_groups - cb), acc);
@@ -654,9 +698,9 @@ __device__ __forceinline__ void mfma_tile(const TileSrc &src, TileBufT<SBG> &buf
 template <int BITS>
 __device__ __forceinline__ void mfma_tile_any(const TileSrc &src, TileBuf &buf, floatx4 &acc) {
   // (4-bit records are row-major: their codes load two groups a load)
-  if (src.m > 8) mfma_tile<BITS, 8, 16, kCodeGroups, BITS == 4>(src, buf, acc);
-  else if (src.m > 4) mfma_tile<BITS, 16, 8, kCodeGroups, BITS == 4>(src, buf, acc);
-  else mfma_tile<BITS, 32, 4, kCodeGroups, BITS == 4>(src, buf, acc);
+  if (src.m > 8) mfma_tile<BITS, 8, 16, kCodeGroups, BITS == 4, true>(src, buf, acc);
+  else if (src.m > 4) mfma_tile<BITS, 16, 8, kCodeGroups, BITS == 4, true>(src, buf, acc);
+  else mfma_tile<BITS, 32, 4, kCodeGroups, BITS == 4, true>(src, buf, acc);
 }
 
 // down: 8 groups of codes in registers and rounds of 8 groups for any m
@@ -664,7 +708,7 @@ __device__ __forceinline__ void mfma_tile_any(const TileSrc &src, TileBuf &buf, 
 // area small enough for four blocks per CU)
 template <int BITS>
 __device__ __forceinline__ void mfma_tile_down(const TileSrc &src, DownBuf &buf, floatx4 &acc) {
-  mfma_tile<BITS, 8, 16, 8, false>(src, buf, acc);
+  mfma_tile<BITS, 8, 16, 8, false, false>(src, buf, acc);
 }
 
 __device__ __forceinline__ void set_brows(const PrefillArgs &a, const Job &j, int *brow, bool act_rows) {
@@ -703,6 +747,7 @@ __global__ __launch_bounds__(kThreads, 3) void pf_gate_up_kernel(PrefillArgs a) 
       src.row_bytes = R.gu_row_bytes;
       src.rows_total = 2 * I;
       src.sb = reinterpret_cast<const uint32_t *>(rec + R.gu_sb);
+      src.sbr = rsrc(rec + R.gu_sb, R.d_codes - R.gu_sb);
       src.sb_group_major = false;
       src.sb_stride = H / kGroup;
       src.bh = a.xf + size_t(2 * order) * kTok * H;
