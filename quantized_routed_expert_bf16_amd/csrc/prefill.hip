@@ -387,19 +387,21 @@ __device__ inline int entry_token_row(const PrefillArgs &a, const Job &j, int n)
 // ------------------------------------------------------- P3 / P4 tiles
 // One work item: 64 output rows (16 per wave) of one sub-job (m <= 16 token
 // rows, one 16-column MFMA tile), over K = n_groups 64-code groups.  The
-// B rows (f16 hi and lo halves, already in MFMA order), the tile's (scale,
-// bias) words and the B rows' group sums go straight from global memory into
-// LDS (global_load_lds: lane i's 16 or 4 bytes land at base + 16 i or 4 i),
-// one round of groups at a time (32 groups for up to 4 rows, 16 for up to 8,
-// 8 for up to 16); the lane's codes for 32 groups load into registers at
-// once.  The buffer is small enough for three blocks per CU, whose load and
-// compute phases interleave.  Token slots past the job's rows hold stale LDS
-// contents: an MFMA output column depends on its own B column only, and
-// those columns are never stored.
+// B rows (f16 hi and lo halves, already in MFMA order) and the B rows' group
+// sums go straight from global memory into LDS (global_load_lds: lane i's 16
+// or 4 bytes land at base + 16 i or 4 i), with the tile's (scale, bias)
+// words (by DMA for group-major records, through registers for row-major
+// ones), one round of groups at a time (gate/up: 32 groups for up to 4 rows,
+// 16 for up to 8, 8 for up to 16; down: 8); the lane's codes for a batch of
+// groups (32 for gate/up, 8 for down) load into registers at once.  The
+// buffers are small enough for three (gate/up) or four (down) blocks per CU,
+// whose load and compute phases interleave.  Token slots past the job's rows
+// hold stale LDS contents: an MFMA output column depends on its own B column
+// only, and those columns are never stored.
 typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
 
-constexpr int kCodeGroups = 32;                 // groups of codes held in registers
+constexpr int kCodeGroups = 32;                 // groups of codes held in registers (gate/up)
 // B area of one round: 16 rows of 8 groups, 8 rows of 16 or 4 rows of 32
 constexpr int kBufHalfs = 16 * (8 * kGroup + 8) > 8 * (16 * kGroup + 8) ? 16 * (8 * kGroup + 8)
                                                                        : 8 * (16 * kGroup + 8);
