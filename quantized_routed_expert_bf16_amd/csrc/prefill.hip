@@ -27,6 +27,8 @@
 // codes of a single 64-code group, so a group's partial sum is scaled after
 // the fact: y += s * sum(q x) + b * sum(x).  The result is as accurate as a
 // float32 dot product; no weight or activation is rounded to f16 as a whole.
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace moe {
@@ -650,32 +652,43 @@ __device__ __forceinline__ void lds_barrier() {
 // the codes as they land.  Later rounds load their operands after the
 // previous round is computed.  Rounds: 32 groups of 4 rows, 16 of 8 or 8
 // of 16.
-template <int BITS, int CG, int ROWS, int KCG, bool PAIR, bool SBROWS, int SBG>
+template <int BITS, int CG, int ROWS, int KCG, bool PAIR, bool SBROWS, int HEAD, int SBG>
 __device__ __forceinline__ void mfma_tile(const TileSrc &src, TileBufT<SBG> &buf, floatx4 &acc) {
   static_assert(ROWS * (CG * kGroup + 8) <= kBufHalfs, "round does not fit the B area");
   static_assert(CG <= SBG && CG <= KCG && ROWS * CG * 2 <= 8 * 16 * 2, "round does not fit the (scale, bias) or sum areas");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int arow = src.r0 + wave * 16 + (lane & 15), g = lane >> 4;
   const int n_groups = src.K / kGroup;
-  constexpr int kCodeLoads = PAIR ? KCG / 2 : (BITS == 3 ? 2 : 1) * KCG;   // the code loads' count
+  // the codes of the batch's first HEAD groups load before round 0's
+  // operands, the rest after them: the wait for the operands then allows
+  // exactly the later codes in flight
+  constexpr int kHead = HEAD;
+  constexpr int kLoadsAfter = PAIR ? (KCG - kHead) / 2 : (BITS == 3 ? 2 : 1) * (KCG - kHead);
+  static_assert(!PAIR || kHead % 2 == 0, "whole pairs before the operands");
   acc = floatx4{0, 0, 0, 0};
   for (int g0 = 0; g0 < n_groups; g0 += KCG) {
     const int nr = (min(KCG, n_groups - g0) + CG - 1) / CG;
+    uint32_t w[KCG][3];
+    auto load_groups = [&](auto qa, auto qb) {   // groups [qa, qb) of the batch
+      if constexpr (PAIR) {
+#pragma unroll
+        for (int P = decltype(qa)::value / 2; P < decltype(qb)::value / 2; ++P)
+          load_codes_pair(src, arow, min(g0 + 2 * P, (n_groups - 1) & ~1), g, w[2 * P], w[2 * P + 1]);
+      } else {
+#pragma unroll
+        for (int Q = decltype(qa)::value; Q < decltype(qb)::value; ++Q)
+          load_codes<BITS>(src, arow, min(g0 + Q, n_groups - 1), g, w[Q]);
+      }
+    };
+    load_groups(std::integral_constant<int, 0>(), std::integral_constant<int, kHead>());
+    asm volatile("" ::: "memory");   // round 0's operands are issued after the first codes
     chunk_dma<CG, !SBROWS>(src, buf, g0, min(CG, n_groups - g0), n_groups);
     SbRun<CG> sbw;
     if constexpr (SBROWS) sb_fetch<CG>(src, g0, sbw);
-    asm volatile("" ::: "memory");   // the codes are issued after round 0's operands
-    uint32_t w[KCG][3];
-    if constexpr (PAIR) {
-#pragma unroll
-      for (int P = 0; P < KCG / 2; ++P)
-        load_codes_pair(src, arow, min(g0 + 2 * P, (n_groups - 1) & ~1), g, w[2 * P], w[2 * P + 1]);
-    } else {
-#pragma unroll
-      for (int Q = 0; Q < KCG; ++Q) load_codes<BITS>(src, arow, min(g0 + Q, n_groups - 1), g, w[Q]);
-    }
-    asm volatile("" ::: "memory");   // ... and all of them before the wait
-    wait_vm<(kCodeLoads < 63 ? kCodeLoads : 63)>();
+    asm volatile("" ::: "memory");   // ... and the remaining codes after them
+    load_groups(std::integral_constant<int, kHead>(), std::integral_constant<int, KCG>());
+    asm volatile("" ::: "memory");   // ... all before the wait
+    wait_vm<(kLoadsAfter < 63 ? kLoadsAfter : 63)>();
     if constexpr (SBROWS) sb_store<CG>(buf, sbw);
     lds_barrier();
 #pragma unroll
@@ -700,17 +713,18 @@ __device__ __forceinline__ void mfma_tile(const TileSrc &src, TileBufT<SBG> &buf
 template <int BITS>
 __device__ __forceinline__ void mfma_tile_any(const TileSrc &src, TileBuf &buf, floatx4 &acc) {
   // (4-bit records are row-major: their codes load two groups a load)
-  if (src.m > 8) mfma_tile<BITS, 8, 16, kCodeGroups, BITS == 4, true>(src, buf, acc);
-  else if (src.m > 4) mfma_tile<BITS, 16, 8, kCodeGroups, BITS == 4, true>(src, buf, acc);
-  else mfma_tile<BITS, 32, 4, kCodeGroups, BITS == 4, true>(src, buf, acc);
+  if (src.m > 8) mfma_tile<BITS, 8, 16, kCodeGroups, BITS == 4, true, 0>(src, buf, acc);
+  else if (src.m > 4) mfma_tile<BITS, 16, 8, kCodeGroups, BITS == 4, true, 0>(src, buf, acc);
+  else mfma_tile<BITS, 32, 4, kCodeGroups, BITS == 4, true, 0>(src, buf, acc);
 }
 
 // down: 8 groups of codes in registers and rounds of 8 groups for any m
 // (K = I is 8 groups at I = 512: one round, and a register budget and LDS
-// area small enough for four blocks per CU)
+// area small enough for four blocks per CU); the first 4 groups' codes load
+// before the round's operands (for gate/up that order measured slower)
 template <int BITS>
 __device__ __forceinline__ void mfma_tile_down(const TileSrc &src, DownBuf &buf, floatx4 &acc) {
-  mfma_tile<BITS, 8, 16, 8, false, false>(src, buf, acc);
+  mfma_tile<BITS, 8, 16, 8, false, false, 4>(src, buf, acc);
 }
 
 __device__ __forceinline__ void set_brows(const PrefillArgs &a, const Job &j, int *brow, bool act_rows) {
