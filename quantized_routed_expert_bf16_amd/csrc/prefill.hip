@@ -308,6 +308,35 @@ __device__ inline uint32_t pair_to_f16(uint32_t v) {
   return __builtin_bit_cast(uint32_t, h - one_k);
 }
 
+// The three masks of the 4-bit expansion, as values the compiler must keep
+// in registers: a mask in a register lets the AND and the OR of a nibble
+// pair fuse into one v_and_or_b32 (a literal cannot be an operand of it).
+struct NibbleMasks {
+  uint32_t lo, hi, ex;   // 0x000F000F, 0x00F000F0, 0x64006400
+};
+__device__ __forceinline__ NibbleMasks nibble_masks() {
+  NibbleMasks m{0x000F000Fu, 0x00F000F0u, 0x64006400u};
+  asm volatile("" : "+v"(m.lo), "+v"(m.hi), "+v"(m.ex));
+  return m;
+}
+
+// One 4-bit code word as eight exact f16 values in the order (0, 4), (1, 5),
+// (2, 6), (3, 7): nibbles at bits 0..3 of a half become 1024 + q and at bits
+// 4..7 1024 + 16 q (exponent bits OR-ed in); one packed f16 add or fma takes
+// them to q exactly.
+__device__ __forceinline__ half8 word4_to_a(uint32_t w, const NibbleMasks &m) {
+  typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+  const half2v k1024 = {_Float16(-1024.0f), _Float16(-1024.0f)};
+  const half2v s16 = {_Float16(0.0625f), _Float16(0.0625f)};
+  const half2v k64 = {_Float16(-64.0f), _Float16(-64.0f)};
+  const uint32_t t = w >> 8;
+  const half2v p0 = __builtin_bit_cast(half2v, (w & m.lo) | m.ex) + k1024;
+  const half2v p1 = __builtin_bit_cast(half2v, (w & m.hi) | m.ex) * s16 + k64;
+  const half2v p2 = __builtin_bit_cast(half2v, (t & m.lo) | m.ex) + k1024;
+  const half2v p3 = __builtin_bit_cast(half2v, (t & m.hi) | m.ex) * s16 + k64;
+  return half8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 template <int BITS>
 __device__ inline void codes_to_a(const uint32_t (&w)[3], half8 (&A)[2], int hshift) {
   uint32_t r[8];
@@ -579,6 +608,7 @@ __device__ __forceinline__ void chunk_mma(const TileSrc &src, const Buf &buf, co
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int partner = (lane ^ 32) * 4;   // ds_bpermute address of slot g ^ 2
   uint32_t ex0 = 0, ex1 = 0;
+  const NibbleMasks nm = nibble_masks();
   // token slot of the lane's B column; when a round stages fewer than 16
   // rows, slots past them (past m) read the staged rows again (their
   // columns are unused)
@@ -596,9 +626,12 @@ __device__ __forceinline__ void chunk_mma(const TileSrc &src, const Buf &buf, co
           ex1 = __builtin_amdgcn_ds_bpermute(partner, w[q0 + Q + 1][1]);
         }
         const bool own = (g >> 1) == (Q & 1);
-        const uint32_t aw[3] = {own ? w[q0 + (Q & ~1)][0] : ex0, own ? w[q0 + (Q & ~1)][1] : ex1, 0u};
-        codes_to_a<BITS>(aw, A, 0);
+        A[0] = word4_to_a(own ? w[q0 + (Q & ~1)][0] : ex0, nm);
+        A[1] = word4_to_a(own ? w[q0 + (Q & ~1)][1] : ex1, nm);
         kb = 16 * (2 * (g & 1) + ((g >> 1) ^ (Q & 1)));
+      } else if constexpr (BITS == 4) {
+        A[0] = word4_to_a(w[q0 + Q][0], nm);
+        A[1] = word4_to_a(w[q0 + Q][1], nm);
       } else {
         codes_to_a<BITS>(w[q0 + Q], A, g & 1);
       }
