@@ -701,15 +701,26 @@ __device__ __forceinline__ void stage_x_fragments(const LayerArgs &a, const floa
 // One 4-bit code word as an A fragment: f16 pairs (0,4), (1,5), (2,6), (3,7).
 // Nibbles at bits 0..3 of a half become 1024 + q and at bits 4..7 1024 + 16q
 // (exponent bits OR-ed in); one packed f16 add or fma takes them to q exactly.
-__device__ __forceinline__ half8 word_to_a(uint32_t w) {
+// The masks come in as register values: with a mask in a register the AND
+// and the OR of a pair fuse into one v_and_or_b32 (a literal cannot be an
+// operand of it).
+struct NibbleMasks {
+  uint32_t lo, hi, ex;   // 0x000F000F, 0x00F000F0, 0x64006400
+};
+__device__ __forceinline__ NibbleMasks nibble_masks() {
+  NibbleMasks m{0x000F000Fu, 0x00F000F0u, 0x64006400u};
+  asm volatile("" : "+v"(m.lo), "+v"(m.hi), "+v"(m.ex));
+  return m;
+}
+__device__ __forceinline__ half8 word_to_a(uint32_t w, const NibbleMasks &m) {
   const half2v k1024 = {_Float16(-1024.0f), _Float16(-1024.0f)};
   const half2v s16 = {_Float16(0.0625f), _Float16(0.0625f)};
   const half2v k64 = {_Float16(-64.0f), _Float16(-64.0f)};
   const uint32_t t = w >> 8;
-  const half2v p0 = __builtin_bit_cast(half2v, (w & 0x000F000Fu) | 0x64006400u) + k1024;
-  const half2v p1 = __builtin_bit_cast(half2v, (w & 0x00F000F0u) | 0x64006400u) * s16 + k64;
-  const half2v p2 = __builtin_bit_cast(half2v, (t & 0x000F000Fu) | 0x64006400u) + k1024;
-  const half2v p3 = __builtin_bit_cast(half2v, (t & 0x00F000F0u) | 0x64006400u) * s16 + k64;
+  const half2v p0 = __builtin_bit_cast(half2v, (w & m.lo) | m.ex) + k1024;
+  const half2v p1 = __builtin_bit_cast(half2v, (w & m.hi) | m.ex) * s16 + k64;
+  const half2v p2 = __builtin_bit_cast(half2v, (t & m.lo) | m.ex) + k1024;
+  const half2v p3 = __builtin_bit_cast(half2v, (t & m.hi) | m.ex) * s16 + k64;
   return half8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
@@ -819,6 +830,7 @@ __device__ __forceinline__ void gate_up_unit_m(const LayerArgs &a, const GuRegsM
   const int partner = (lane ^ 32) * 4;   // ds_bpermute address of slot q ^ 2
   const uint4 z = make_uint4(0, 0, 0, 0);
   uint32_t ex0 = 0, ex1 = 0;
+  const NibbleMasks nm = nibble_masks();
   floatx4 tot = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int gi = 0; gi < kMGw; ++gi) {
@@ -846,8 +858,8 @@ __device__ __forceinline__ void gate_up_unit_m(const LayerArgs &a, const GuRegsM
         w0 = own ? v.x : ex0;
         w1 = own ? v.y : ex1;
       }
-      A0 = word_to_a(w0);
-      A1 = word_to_a(w1);
+      A0 = word_to_a(w0, nm);
+      A1 = word_to_a(w1, nm);
     } else {
       // the slot's word of the group (codes 16 wq .. + 15) and, 3-bit, the
       // high bits of those codes: nibble wq % 2 of each byte of the high
@@ -1265,6 +1277,7 @@ __device__ __forceinline__ void run_down_m(const LayerArgs &a, Shared<NB> &sh, i
     }
     __syncthreads();
     // 4. the wave's slots
+    const NibbleMasks nm = nibble_masks();
 #pragma unroll
     for (int m = 0; m < kDownSlots; ++m) {
       const int sl = par + 2 * m, slot = s0 + sl;
@@ -1272,8 +1285,8 @@ __device__ __forceinline__ void run_down_m(const LayerArgs &a, Shared<NB> &sh, i
       if (bt == 0) continue;
       half8 A0, A1;
       if (bt == 4) {
-        A0 = word_to_a(cw[m].x);
-        A1 = word_to_a(cw[m].y);
+        A0 = word_to_a(cw[m].x, nm);
+        A1 = word_to_a(cw[m].y, nm);
       } else {
         // 3-bit: the high bits of the slot word's codes are nibble q % 2 of
         // each byte of its chunk's high word
