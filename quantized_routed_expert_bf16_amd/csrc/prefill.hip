@@ -601,57 +601,64 @@ __device__ __forceinline__ void sb_store(Buf &buf, const SbRun<CG> &r) {
 // of group Q with kb = 16 (2 (g & 1) + ((g >> 1) ^ (Q & 1))), its own lower
 // words when (g >> 1) == (Q & 1) and the received ones otherwise; the B
 // fragments are read at the same kb.
+// Group Q of the round whose first group is batch group q0; on the paired
+// path the even group of a pair receives both groups' exchanged words
+// (ex0, ex1) for the odd one.
 template <int BITS, int CG, int ROWS, int KCG, bool PAIR, class Buf>
-__device__ __forceinline__ void chunk_mma(const TileSrc &src, const Buf &buf, const uint32_t (&w)[KCG][3],
-                                          int q0, int gq, floatx4 &acc) {
+__device__ __forceinline__ void group_mma(const TileSrc &src, const Buf &buf, const uint32_t (&w)[KCG][3],
+                                          int q0, int Q, floatx4 &acc, const NibbleMasks &nm,
+                                          uint32_t &ex0, uint32_t &ex1) {
   static_assert(!PAIR || (BITS == 4 && CG % 2 == 0), "paired loads: 4-bit codes, whole pairs a round");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int partner = (lane ^ 32) * 4;   // ds_bpermute address of slot g ^ 2
-  uint32_t ex0 = 0, ex1 = 0;
-  const NibbleMasks nm = nibble_masks();
   // token slot of the lane's B column; when a round stages fewer than 16
   // rows, slots past them (past m) read the staged rows again (their
   // columns are unused)
   static_assert(ROWS == 4 || ROWS == 8 || ROWS == 16, "rounds stage 4, 8 or 16 token rows");
   const int g = lane >> 4, n = lane & (ROWS - 1);
   constexpr int kRow = CG * kGroup + 8;
-#pragma unroll
-  for (int Q = 0; Q < CG; ++Q) {
-    if (Q < gq) {
-      half8 A[2];
-      int kb = 16 * g;   // first of the lane's 16 codes of group Q
-      if constexpr (PAIR) {
-        if ((Q & 1) == 0) {   // one exchange serves both groups of the pair
-          ex0 = __builtin_amdgcn_ds_bpermute(partner, w[q0 + Q + 1][0]);
-          ex1 = __builtin_amdgcn_ds_bpermute(partner, w[q0 + Q + 1][1]);
-        }
-        const bool own = (g >> 1) == (Q & 1);
-        A[0] = word4_to_a(own ? w[q0 + (Q & ~1)][0] : ex0, nm);
-        A[1] = word4_to_a(own ? w[q0 + (Q & ~1)][1] : ex1, nm);
-        kb = 16 * (2 * (g & 1) + ((g >> 1) ^ (Q & 1)));
-      } else if constexpr (BITS == 4) {
-        A[0] = word4_to_a(w[q0 + Q][0], nm);
-        A[1] = word4_to_a(w[q0 + Q][1], nm);
-      } else {
-        codes_to_a<BITS>(w[q0 + Q], A, g & 1);
-      }
-      const uint4 sq = *static_cast<const uint4 *>(__builtin_assume_aligned(buf.sb + Q * 64 + wave * 16 + 4 * g, 16));
-      const uint32_t sw4[4] = {sq.x, sq.y, sq.z, sq.w};
-      floatx4 cgv = {0, 0, 0, 0};
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int at = n * kRow + Q * kGroup + kb + 8 * st;
-        const half8 Bh = *static_cast<const half8 *>(__builtin_assume_aligned(buf.bh + at, 16));
-        const half8 Bl = *static_cast<const half8 *>(__builtin_assume_aligned(buf.bl + at, 16));
-        cgv = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[st], Bh, cgv, 0, 0, 0);
-        cgv = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[st], Bl, cgv, 0, 0, 0);
-      }
-      const float *xp = buf.xs + (n * CG + Q) * src.parts;
-      const float xs = src.parts == 2 ? xp[0] + xp[1] : xp[0];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = fmaf(sb_scale(sw4[q]), cgv[q], fmaf(sb_bias(sw4[q]), xs, acc[q]));
+  half8 A[2];
+  int kb = 16 * g;   // first of the lane's 16 codes of group Q
+  if constexpr (PAIR) {
+    if ((Q & 1) == 0) {   // one exchange serves both groups of the pair
+      const int partner = (lane ^ 32) * 4;   // ds_bpermute address of slot g ^ 2
+      ex0 = __builtin_amdgcn_ds_bpermute(partner, w[q0 + Q + 1][0]);
+      ex1 = __builtin_amdgcn_ds_bpermute(partner, w[q0 + Q + 1][1]);
     }
+    const bool own = (g >> 1) == (Q & 1);
+    A[0] = word4_to_a(own ? w[q0 + (Q & ~1)][0] : ex0, nm);
+    A[1] = word4_to_a(own ? w[q0 + (Q & ~1)][1] : ex1, nm);
+    kb = 16 * (2 * (g & 1) + ((g >> 1) ^ (Q & 1)));
+  } else if constexpr (BITS == 4) {
+    A[0] = word4_to_a(w[q0 + Q][0], nm);
+    A[1] = word4_to_a(w[q0 + Q][1], nm);
+  } else {
+    codes_to_a<BITS>(w[q0 + Q], A, g & 1);
   }
+  const uint4 sq = *static_cast<const uint4 *>(__builtin_assume_aligned(buf.sb + Q * 64 + wave * 16 + 4 * g, 16));
+  const uint32_t sw4[4] = {sq.x, sq.y, sq.z, sq.w};
+  floatx4 cgv = {0, 0, 0, 0};
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const int at = n * kRow + Q * kGroup + kb + 8 * st;
+    const half8 Bh = *static_cast<const half8 *>(__builtin_assume_aligned(buf.bh + at, 16));
+    const half8 Bl = *static_cast<const half8 *>(__builtin_assume_aligned(buf.bl + at, 16));
+    cgv = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[st], Bh, cgv, 0, 0, 0);
+    cgv = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[st], Bl, cgv, 0, 0, 0);
+  }
+  const float *xp = buf.xs + (n * CG + Q) * src.parts;
+  const float xs = src.parts == 2 ? xp[0] + xp[1] : xp[0];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q] = fmaf(sb_scale(sw4[q]), cgv[q], fmaf(sb_bias(sw4[q]), xs, acc[q]));
+}
+
+// The first gq groups of the round.
+template <int BITS, int CG, int ROWS, int KCG, bool PAIR, class Buf>
+__device__ __forceinline__ void chunk_mma(const TileSrc &src, const Buf &buf, const uint32_t (&w)[KCG][3],
+                                          int q0, int gq, floatx4 &acc, const NibbleMasks &nm) {
+  uint32_t ex0 = 0, ex1 = 0;
+#pragma unroll
+  for (int Q = 0; Q < CG; ++Q)
+    if (Q < gq) group_mma<BITS, CG, ROWS, KCG, PAIR>(src, buf, w, q0, Q, acc, nm, ex0, ex1);
 }
 
 // s_waitcnt on the vector-memory count only: at most N loads of this wave
@@ -679,13 +686,16 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // The rounds of a work item, with an early start: round 0's operands go to
-// LDS first, then every code of the batch loads in group order, and round 0
-// waits only for its operands (the codes are the loads issued after them,
-// and the counter retires loads in issue order); its groups then consume
-// the codes as they land.  Later rounds load their operands after the
-// previous round is computed.  Rounds: 32 groups of 4 rows, 16 of 8 or 8
-// of 16.
-template <int BITS, int CG, int ROWS, int KCG, bool PAIR, bool SBROWS, int HEAD, int SBG>
+// LDS first, then the codes of the batch's first PRE groups load in group
+// order, and round 0 waits only for its operands (the codes are the loads
+// issued after them, and the counter retires loads in issue order); its
+// groups then consume the codes as they land, and on the paired path each
+// computed pair of groups issues the loads of the next pair not yet in
+// flight, so that a wave computes between its load issues instead of
+// stalling on a full memory queue with every load of the item still to
+// issue.  Later rounds load their operands after the previous round is
+// computed.  Rounds: 32 groups of 4 rows, 16 of 8 or 8 of 16.
+template <int BITS, int CG, int ROWS, int KCG, bool PAIR, bool SBROWS, int HEAD, int SBG, int PRE = KCG>
 __device__ __forceinline__ void mfma_tile(const TileSrc &src, TileBufT<SBG> &buf, floatx4 &acc) {
   static_assert(ROWS * (CG * kGroup + 8) <= kBufHalfs, "round does not fit the B area");
   static_assert(CG <= SBG && CG <= KCG && ROWS * CG * 2 <= 8 * 16 * 2, "round does not fit the (scale, bias) or sum areas");
@@ -696,8 +706,11 @@ __device__ __forceinline__ void mfma_tile(const TileSrc &src, TileBufT<SBG> &buf
   // operands, the rest after them: the wait for the operands then allows
   // exactly the later codes in flight
   constexpr int kHead = HEAD;
-  constexpr int kLoadsAfter = PAIR ? (KCG - kHead) / 2 : (BITS == 3 ? 2 : 1) * (KCG - kHead);
-  static_assert(!PAIR || kHead % 2 == 0, "whole pairs before the operands");
+  constexpr int kPre = PAIR ? PRE : KCG;   // groups whose codes load before round 0 computes
+  constexpr int kLoadsAfter = PAIR ? (kPre - kHead) / 2 : (BITS == 3 ? 2 : 1) * (KCG - kHead);
+  static_assert(!PAIR || (kHead % 2 == 0 && kPre % 2 == 0), "whole pairs before the operands");
+  static_assert(kPre >= kHead && kPre <= KCG, "the first loads are a prefix of the batch");
+  const NibbleMasks nm = nibble_masks();
   acc = floatx4{0, 0, 0, 0};
   for (int g0 = 0; g0 < n_groups; g0 += KCG) {
     const int nr = (min(KCG, n_groups - g0) + CG - 1) / CG;
@@ -719,7 +732,7 @@ __device__ __forceinline__ void mfma_tile(const TileSrc &src, TileBufT<SBG> &buf
     SbRun<CG> sbw;
     if constexpr (SBROWS) sb_fetch<CG>(src, g0, sbw);
     asm volatile("" ::: "memory");   // ... and the remaining codes after them
-    load_groups(std::integral_constant<int, kHead>(), std::integral_constant<int, KCG>());
+    load_groups(std::integral_constant<int, kHead>(), std::integral_constant<int, kPre>());
     asm volatile("" ::: "memory");   // ... all before the wait
     wait_vm<(kLoadsAfter < 63 ? kLoadsAfter : 63)>();
     if constexpr (SBROWS) sb_store<CG>(buf, sbw);
@@ -736,19 +749,41 @@ __device__ __forceinline__ void mfma_tile(const TileSrc &src, TileBufT<SBG> &buf
           if constexpr (SBROWS) sb_store<CG>(buf, sbw);
           lds_barrier();
         }
-        chunk_mma<BITS, CG, ROWS, KCG, PAIR>(src, buf, w, cs * CG, min(CG, n_groups - cb), acc);
+        if (kPre < KCG && cs == 0) {
+          const int gq = min(CG, n_groups - cb);
+          uint32_t ex0 = 0, ex1 = 0;
+#pragma unroll
+          for (int P = 0; P < CG / 2; ++P) {
+            if (2 * P < gq) group_mma<BITS, CG, ROWS, KCG, PAIR>(src, buf, w, 0, 2 * P, acc, nm, ex0, ex1);
+            if (2 * P + 1 < gq) group_mma<BITS, CG, ROWS, KCG, PAIR>(src, buf, w, 0, 2 * P + 1, acc, nm, ex0, ex1);
+            if (kPre / 2 + P < KCG / 2) {
+              asm volatile("" ::: "memory");   // issued after the pair's operand reads
+              const int L = kPre / 2 + P;
+              load_codes_pair(src, arow, min(g0 + 2 * L, (n_groups - 1) & ~1), g, w[2 * L], w[2 * L + 1]);
+            }
+          }
+          // pairs still unissued go before the next round's operands
+          load_groups(std::integral_constant<int, (kPre + CG < KCG ? kPre + CG : KCG)>(),
+                      std::integral_constant<int, KCG>());
+        } else {
+          chunk_mma<BITS, CG, ROWS, KCG, PAIR>(src, buf, w, cs * CG, min(CG, n_groups - cb), acc, nm);
+        }
       }
     }
     __syncthreads();   // the buffer is free for the next batch or work item
   }
 }
 
+constexpr int kPreGroups = 8;   // gate/up: groups whose codes load before round 0 computes
+
 template <int BITS>
 __device__ __forceinline__ void mfma_tile_any(const TileSrc &src, TileBuf &buf, floatx4 &acc) {
   // (4-bit records are row-major: their codes load two groups a load)
-  if (src.m > 8) mfma_tile<BITS, 8, 16, kCodeGroups, BITS == 4, true, 0>(src, buf, acc);
-  else if (src.m > 4) mfma_tile<BITS, 16, 8, kCodeGroups, BITS == 4, true, 0>(src, buf, acc);
-  else mfma_tile<BITS, 32, 4, kCodeGroups, BITS == 4, true, 0>(src, buf, acc);
+  constexpr bool kPair = BITS == 4;
+  constexpr int kPre = kPair ? kPreGroups : kCodeGroups;
+  if (src.m > 8) mfma_tile<BITS, 8, 16, kCodeGroups, kPair, true, 0, 32, kPre>(src, buf, acc);
+  else if (src.m > 4) mfma_tile<BITS, 16, 8, kCodeGroups, kPair, true, 0, 32, kPre>(src, buf, acc);
+  else mfma_tile<BITS, 32, 4, kCodeGroups, kPair, true, 0, 32, kPre>(src, buf, acc);
 }
 
 // down: 8 groups of codes in registers and rounds of 8 groups for any m
