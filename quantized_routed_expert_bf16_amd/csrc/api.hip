@@ -84,7 +84,7 @@ WorkspaceLayout workspace_layout(int hidden, int inter, int n_experts, int top_k
   w.pf_act = take(size_t(2) * w.pf_act_rows * inter * sizeof(_Float16));
   w.pf_asum = take(size_t(w.pf_act_rows) * (inter / 32) * sizeof(float));
   w.pf_y = take(size_t(pf_rows) * (top_k + 1) * hidden * sizeof(float));
-  w.pf_meta = take(size_t(1 + 2 * (2 * kMaxExperts + 2)) * sizeof(int32_t));
+  w.pf_meta = take(size_t(kJobInts) * (1 + 2 * kMaxExperts + 2) * sizeof(int32_t));
   w.total = pos;
   return w;
 }

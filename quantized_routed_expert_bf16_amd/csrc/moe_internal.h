@@ -17,6 +17,7 @@ constexpr int kSlotStride = MOE_SLOT_STRIDE;
 constexpr int kMaxNb = MOE_MAX_NB;
 constexpr int kSharedSlot = 63;   // act / partial index used for the shared expert
 constexpr int kMaxExperts = 256;
+constexpr int kJobInts = 8;   // prefill sub-job record (ints), after a header of the same size
 constexpr int kMaxTopK = 15;
 
 // ----------------------------------------------------------- record layout
@@ -83,7 +84,7 @@ struct WorkspaceLayout {
   int pf_act_rows;     // entries pf_act holds
   size_t pf_asum;      // prefill: [t*k + t][I/32] f32 sums of 32-column act blocks
   size_t pf_y;         // prefill: [t][k+1][H] f32 weighted outputs per (row, rank)
-  size_t pf_meta;      // prefill: sub-job count, then (expert, first row) pairs
+  size_t pf_meta;      // prefill: sub-job count, then one 32-byte record per sub-job
   size_t total;
 };
 
@@ -131,7 +132,8 @@ struct PrefillArgs {
   float *asum;                 // [act_rows][I/32] sums of act over 32-column blocks
   int act_rows;                // entries the act buffer holds (shared entries last)
   float *y;                    // [t][k+1][H] weighted output per (row, rank); rank k = shared
-  int32_t *meta;               // sub-job count, then (expert or -1, first row) per sub-job
+  int32_t *meta;               // [0] sub-job count; sub-job s at 8 + 8 s: expert (-1 = shared),
+                               // first entry | rows << 16, descriptor, token row of each slot (bytes)
   uint32_t *status;
   float *out;                  // [t][H]
 };

@@ -47,11 +47,11 @@ constexpr int kTok = MOE_MAX_PREFILL_ROWS;   // 32 token slots per expert
 // q + 4 of a word) and order 1 (2/3-bit records: fields q and q + 8) follow
 // from how the codes unpack into f16 pairs; x and act are stored in the same
 // order so that a lane's B fragment is 16 contiguous bytes.
-__host__ __device__ constexpr int frag_code(int order, int p) {
+__host__ __device__ __forceinline__ constexpr int frag_code(int order, int p) {
   return order == 0 ? 8 * (p >> 3) + ((p & 7) >> 1) + 4 * (p & 1)
                     : 4 * (p >> 3) + ((p & 7) >> 1) + 8 * (p & 1);
 }
-__host__ __device__ constexpr int frag_pos(int order, int c) {   // inverse of frag_code
+__host__ __device__ __forceinline__ constexpr int frag_pos(int order, int c) {   // inverse of frag_code
   return order == 0 ? 8 * (c >> 3) + 2 * ((c & 7) & 3) + ((c & 7) >> 2)
                     : 8 * ((c & 7) >> 2) + 2 * (c & 3) + (c >> 3);
 }
@@ -178,10 +178,16 @@ __global__ __launch_bounds__(128) void pf_topk_kernel(PrefillArgs a, const doubl
   __shared__ int cnt[kMaxExperts + 1];
   __shared__ uint32_t emask[kMaxExperts];
   __shared__ int wsum[2];
+  __shared__ int sjx[kMaxExperts];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int E = a.n_experts, k = a.top_k, t = a.t;
   const int r = blockIdx.x;
   const int Ep = (E + 7) & ~7;
+  // the descriptors of experts threadIdx.x and threadIdx.x + 128, for the
+  // sub-job records in case this block is the last (loaded with the logits,
+  // so that the last block does not wait for them)
+  const uint64_t rv0 = a.rec[min(int(threadIdx.x), E - 1)];
+  const uint64_t rv1 = a.rec[min(int(threadIdx.x) + 128, E - 1)];
   // logits (+ 0.0 folds -0 into +0, so equal values tie on the id alone) and
   // 32-bit order keys of them rounded to float32; padding keys are 0, below
   // every logit's key
@@ -258,38 +264,48 @@ __global__ __launch_bounds__(128) void pf_topk_kernel(PrefillArgs a, const doubl
     if (threadIdx.x == 0) cnt[E] = wsum[0] + wsum[1];
   }
   __syncthreads();
-  // sub-jobs (expert, first row), longest first: the shared expert's, then
-  // the heavy experts', then the light ones' (experts ascending in each), so
-  // that the items with the most rounds start their loads first
+  // sub-jobs (at most 16 rows each), longest first: the shared expert's,
+  // then the heavy experts', then the light ones' (experts ascending in
+  // each), so that the items with the most rounds start their loads first.
+  // Each gets a record: expert, first entry and rows, descriptor, and the
+  // token row of each slot (written with the entries below), so that a work
+  // item finds all it needs in one load.
   const int n_shared = t > 16 ? 2 : 1, n_heavy = (cnt[E] >> 10) & 1023;
+  auto job_rec = [&](int sj, int e, int base, int m, uint64_t d) {
+    int32_t *jr = a.meta + kJobInts * (1 + sj);
+    jr[0] = e;
+    jr[1] = base | (m << 16);
+    jr[2] = int32_t(uint32_t(d));
+    jr[3] = int32_t(uint32_t(d >> 32));
+  };
   for (int e = threadIdx.x; e <= E; e += 128) {
     const int v = cnt[e];
     expert_ptr[e] = v >> 20;
     if (e < E && emask[e]) {
       const int c = __popc(emask[e]);
       const int sj = c > 8 ? n_shared + ((v >> 10) & 1023) : n_shared + n_heavy + (v & 1023);
-      a.meta[1 + 2 * sj] = e;
-      a.meta[2 + 2 * sj] = 0;
-      if (c > 16) {
-        a.meta[3 + 2 * sj] = e;
-        a.meta[4 + 2 * sj] = 16;
-      }
+      const uint64_t d = e == int(threadIdx.x) ? rv0 : rv1;
+      sjx[e] = sj;
+      job_rec(sj, e, v >> 20, min(c, 16), d);
+      if (c > 16) job_rec(sj + 1, e, (v >> 20) + 16, c - 16, d);
     }
   }
   if (threadIdx.x == 0) {
-    a.meta[1] = -1;
-    a.meta[2] = 0;
-    if (t > 16) {
-      a.meta[3] = -1;
-      a.meta[4] = 16;
+    for (int h = 0; h < n_shared; ++h) {
+      job_rec(h, -1, t * k + 16 * h, min(t - 16 * h, 16), a.shared_rec);
+      uint32_t *rows = reinterpret_cast<uint32_t *>(a.meta + kJobInts * (1 + h) + 4);
+      for (int i = 0; i < 4; ++i)
+        rows[i] = uint32_t(16 * h + 4 * i) * 0x01010101u + 0x03020100u;
     }
     a.meta[0] = n_shared + n_heavy + (cnt[E] & 1023);
   }
+  __syncthreads();
   for (int p = threadIdx.x; p < t * k; p += 128) {
     const int e = all_sel[p], r = p / k;
-    const int pos = (cnt[e] >> 20) + __popc(emask[e] & ((1u << r) - 1u));
+    const int q = __popc(emask[e] & ((1u << r) - 1u)), pos = (cnt[e] >> 20) + q;
     entry_row[pos] = r;
     entry_rank[pos] = p - r * k;
+    reinterpret_cast<uint8_t *>(a.meta + kJobInts * (1 + sjx[e] + (q >> 4)) + 4)[q & 15] = uint8_t(r);
   }
   if (threadIdx.x == 0) st_dev(counter, 0u);
 }
@@ -391,23 +407,26 @@ struct Job {
   int base;     // first entry index of its rows
   int m;        // rows (1..16)
   uint64_t desc;
+  int lane_row;       // lane n < m: token row of slot n
 };
 
-__device__ inline bool job_of(const PrefillArgs &a, int sj, Job &j) {
-  if (sj >= a.meta[0]) return false;
-  j.e = a.meta[1 + 2 * sj];
-  const int off = a.meta[2 + 2 * sj];
-  if (j.e >= 0) {
-    const int b0 = a.expert_ptr[j.e];
-    j.base = b0 + off;
-    j.m = min(16, a.expert_ptr[j.e + 1] - b0 - off);
-    j.desc = a.rec[j.e];
-  } else {
-    j.base = a.t * a.top_k + off;
-    j.m = min(16, a.t - off);
-    j.desc = a.shared_rec;
-  }
-  return true;
+// the record of sub-job sj (below the workspace's capacity of sub-jobs)
+__device__ inline Job job_of(const PrefillArgs &a, int sj) {
+  typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+  const i32x8 r = *reinterpret_cast<const i32x8 *>(a.meta + kJobInts * (1 + sj));
+  Job j;
+  j.e = __builtin_amdgcn_readfirstlane(r[0]);
+  const int bm = __builtin_amdgcn_readfirstlane(r[1]);
+  j.base = bm & 0xffff;
+  j.m = bm >> 16;
+  j.desc = uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(r[2]))) |
+           (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(r[3]))) << 32);
+  // byte n of words 4..7 (slots past the job's rows hold stale bytes, never used)
+  const int n = threadIdx.x & 15;
+  const uint32_t w01 = (n & 4) ? uint32_t(r[5]) : uint32_t(r[4]);
+  const uint32_t w23 = (n & 4) ? uint32_t(r[7]) : uint32_t(r[6]);
+  j.lane_row = int((((n & 8) ? w23 : w01) >> (8 * (n & 3))) & 255u);
+  return j;
 }
 
 // token row of a sub-job's n-th entry
@@ -462,7 +481,7 @@ struct TileSrc {
   int K;                  // codes per row = 64 n_groups
   int r0;                 // first of the tile's 64 rows
   int m;                  // token rows of the job (<= 16)
-  const int *brow;        // LDS: B row of each token slot
+  int lane_brow;          // lane n < m: the B row of token slot n (other lanes: unused)
 };
 
 // A buffer resource built from wave-uniform parts (readfirstlane), so that
@@ -518,9 +537,7 @@ __device__ __forceinline__ void chunk_dma(const TileSrc &src, Buf &buf, int g0, 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int kRow = CG * kGroup + 8;            // B row stride in LDS (halfs)
   constexpr int kSegs = CG * kGroup / 512;         // 1 KB segments per B row
-  // the B row of token slot n is lane n's: read from LDS once, before any
-  // DMA load (an LDS read behind a DMA load in flight waits for it)
-  const int lane_brow = src.brow[min(lane, src.m - 1)];
+  const int lane_brow = src.lane_brow;   // the B row of token slot n is lane n's
   // B rows: one load per (token row, hi/lo, segment)
   for (int q = wave; q < 2 * kSegs * src.m; q += kWaves) {
     const int n = q / (2 * kSegs), hl = (q / kSegs) & 1, seg = q % kSegs;
@@ -795,10 +812,6 @@ __device__ __forceinline__ void mfma_tile_down(const TileSrc &src, DownBuf &buf,
   mfma_tile<BITS, 8, 16, 8, false, false, 4>(src, buf, acc);
 }
 
-__device__ __forceinline__ void set_brows(const PrefillArgs &a, const Job &j, int *brow, bool act_rows) {
-  for (int n = threadIdx.x; n < j.m; n += kThreads)
-    brow[n] = act_rows ? j.base + n : entry_token_row(a, j, n);
-}
 
 // ------------------------------------------------------------------ P3
 // gate/up: work item (job, 64 interleaved gate/up rows); act = silu(g) * u
@@ -807,24 +820,22 @@ __device__ __forceinline__ void set_brows(const PrefillArgs &a, const Job &j, in
 // term.
 __global__ __launch_bounds__(kThreads, 3) void pf_gate_up_kernel(PrefillArgs a) {
   __shared__ TileBuf buf;
-  __shared__ int brow[16];
   __shared__ float red[kWaves][16];
   const int H = a.hidden, I = a.inter;
-  const int tiles = 2 * I / 64;
+  // grid: (tile, sub-job); the first item's record loads with the sub-job
+  // count (gridDim.y never exceeds the records the workspace holds)
+  const int tile = blockIdx.x;
   const int n_jobs = a.meta[0];
+  Job j = job_of(a, blockIdx.y);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, nl = lane & 15;
-  for (int w = blockIdx.x; w < n_jobs * tiles; w += gridDim.x) {
-    Job j;
-    if (!job_of(a, w / tiles, j)) break;
-    const int tile = w % tiles;
+  for (int sj = blockIdx.y; sj < n_jobs; sj += gridDim.y) {
+    if (sj != int(blockIdx.y)) j = job_of(a, sj);
     const bool ok = record_ok(j.desc, a.pool_bytes, H, I);
     const int bits = ok ? bits_of_tag(j.desc) : 4, order = bits == 4 ? 0 : 1;
     floatx4 acc = {0, 0, 0, 0};
     if (ok) {
       const RecordLayout R = record_layout(H, I, bits);
       const uint8_t *rec = a.pool + (j.desc & ~uint64_t(255));
-      set_brows(a, j, brow, false);
-      __syncthreads();
       TileSrc src;
       src.codes = rsrc(rec + R.gu_codes, R.gu_sb - R.gu_codes);
       src.group_major = false;
@@ -841,7 +852,7 @@ __global__ __launch_bounds__(kThreads, 3) void pf_gate_up_kernel(PrefillArgs a) 
       src.K = H;
       src.r0 = tile * 64;
       src.m = j.m;
-      src.brow = brow;
+      src.lane_brow = j.lane_row;
       switch (bits) {
         case 4: mfma_tile_any<4>(src, buf, acc); break;
         case 3: mfma_tile_any<3>(src, buf, acc); break;
@@ -886,23 +897,19 @@ __global__ __launch_bounds__(kThreads, 3) void pf_gate_up_kernel(PrefillArgs a) 
 // every (row, rank) entry of the job.
 __global__ __launch_bounds__(kThreads) void pf_down_kernel(PrefillArgs a) {
   __shared__ DownBuf buf;
-  __shared__ int brow[16];
   const int H = a.hidden, I = a.inter;
-  const int tiles = H / 64;
+  const int tile = blockIdx.x;   // grid: (tile, sub-job)
   const int n_jobs = a.meta[0];
+  Job j = job_of(a, blockIdx.y);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, nl = lane & 15;
-  for (int w = blockIdx.x; w < n_jobs * tiles; w += gridDim.x) {
-    Job j;
-    if (!job_of(a, w / tiles, j)) break;
-    const int tile = w % tiles;
+  for (int sj = blockIdx.y; sj < n_jobs; sj += gridDim.y) {
+    if (sj != int(blockIdx.y)) j = job_of(a, sj);
     const bool ok = record_ok(j.desc, a.pool_bytes, H, I);
     floatx4 acc = {0, 0, 0, 0};
     if (ok) {
       const int bits = bits_of_tag(j.desc);
       const RecordLayout R = record_layout(H, I, bits);
       const uint8_t *rec = a.pool + (j.desc & ~uint64_t(255));
-      set_brows(a, j, brow, true);
-      __syncthreads();
       TileSrc src;
       src.codes = rsrc(rec + R.d_codes, R.d_sb - R.d_codes);
       src.group_major = true;
@@ -918,7 +925,7 @@ __global__ __launch_bounds__(kThreads) void pf_down_kernel(PrefillArgs a) {
       src.K = I;
       src.r0 = tile * 64;
       src.m = j.m;
-      src.brow = brow;
+      src.lane_brow = j.base + min(lane, j.m - 1);   // the job's act rows
       switch (bits) {
         case 4: mfma_tile_down<4>(src, buf, acc); break;
         case 3: mfma_tile_down<3>(src, buf, acc); break;
@@ -943,7 +950,6 @@ __global__ __launch_bounds__(kThreads) void pf_down_kernel(PrefillArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) dst[q] = ok ? wgt * acc[q] : 0.0f;
     }
-    __syncthreads();   // brow is rewritten by the next work item
   }
 }
 
@@ -995,12 +1001,15 @@ hipError_t launch_prefill(const PrefillArgs &a, const uint16_t *router, const ui
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = mark(0)) != hipSuccess) return e;
   const int max_jobs = min(a.n_experts, a.t * a.top_k) + 1;
-  const int gu_grid = min(max_jobs * (2 * a.inter / 64), 1024);
-  hipLaunchKernelGGL(pf_gate_up_kernel, dim3(gu_grid), dim3(kThreads), 0, s, a);
+  // (tile, sub-job) grids of at most 1024 blocks; sub-jobs past the count
+  // exit at once, and those past the grid are taken in strides
+  const int gu_tiles = 2 * a.inter / 64, d_tiles = a.hidden / 64;
+  const dim3 gu_grid(gu_tiles, min(max_jobs, max(1, 1024 / gu_tiles)));
+  hipLaunchKernelGGL(pf_gate_up_kernel, gu_grid, dim3(kThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = mark(1)) != hipSuccess) return e;
-  const int d_grid = min(max_jobs * (a.hidden / 64), 1024);
-  hipLaunchKernelGGL(pf_down_kernel, dim3(d_grid), dim3(kThreads), 0, s, a);
+  const dim3 d_grid(d_tiles, min(max_jobs, max(1, 1024 / d_tiles)));
+  hipLaunchKernelGGL(pf_down_kernel, d_grid, dim3(kThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = mark(2)) != hipSuccess) return e;
   const int c_grid = min((a.t * a.hidden / 4 + kCombineThreads - 1) / kCombineThreads, 4096);
