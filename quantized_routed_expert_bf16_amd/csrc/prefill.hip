@@ -13,7 +13,8 @@
 //      hi/lo split of x plus per-64 group sums of x;
 //   P2 per-row top-k and weights; the last block groups the rows by expert
 //      (experts ascending, rows ascending) and lists the sub-jobs (at most
-//      16 rows of one expert), longest first;
+//      16 rows of one expert), longest first, one record each (expert,
+//      entries, descriptor, token rows) that a work item reads in one load;
 //   P3 gate/up: per (used expert, 64 gate/up rows), MFMA 16x16x32 f16 tiles
 //      of 16 rows x 16 tokens (1 or 2 token tiles for m <= 16 or <= 32);
 //   P4 down: per (used expert, 64 output rows), same tiles, writes the
