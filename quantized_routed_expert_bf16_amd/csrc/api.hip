@@ -365,6 +365,7 @@ int moe_prefill_forward(const float *x, int32_t t, const moe_router *router, moe
   pa.x = x;
   pa.rec = router->rec;
   pa.shared_rec = shared->rec;
+  pa.topk_idx = plan->topk_idx;
   pa.expert_ptr = plan->expert_ptr;
   pa.entry_row = plan->entry_row;
   pa.entry_rank = plan->entry_rank;

@@ -120,9 +120,10 @@ struct PrefillArgs {
   const float *x;              // [t][H]
   const uint64_t *rec;         // [E]
   uint64_t shared_rec;
-  const int32_t *expert_ptr;   // [E+1]
-  const int32_t *entry_row;    // [t*k]
-  const int32_t *entry_rank;   // [t*k]
+  const uint32_t *topk_idx;    // [t][k]
+  int32_t *expert_ptr;         // [E+1]  (written by the gate/up pass)
+  int32_t *entry_row;          // [t*k]
+  int32_t *entry_rank;         // [t*k]
   float *topk_w;               // [t][k]
   const float *gamma;          // [t]
   int hidden, inter, n_experts, top_k, t;
@@ -133,7 +134,8 @@ struct PrefillArgs {
   int act_rows;                // entries the act buffer holds (shared entries last)
   float *y;                    // [t][k+1][H] weighted output per (row, rank); rank k = shared
   int32_t *meta;               // [0] sub-job count; sub-job s at 8 + 8 s: expert (-1 = shared),
-                               // first entry | rows << 16, descriptor, token row of each slot (bytes)
+                               // first entry | rows << 16, descriptor, token row of each slot
+                               // (bytes); written by the gate/up pass for the down pass
   uint32_t *status;
   float *out;                  // [t][H]
 };

@@ -166,29 +166,18 @@ __global__ __launch_bounds__(kThreads) void pf_router_kernel(PrefillArgs a, cons
 }
 
 // ------------------------------------------------------------------ P2
-__global__ __launch_bounds__(128) void pf_topk_kernel(PrefillArgs a, const double *logits,
-                                                      uint32_t *topk_idx, uint32_t *counter,
-                                                      int32_t *expert_ptr, int32_t *entry_row,
-                                                      int32_t *entry_rank) {
+// One block a row: the row's top k (logit descending, id ascending) and
+// their softmax weights.  The grouping of the rows by expert is rebuilt by
+// every block of the gate/up pass from these ids (no cross-block step here).
+__global__ __launch_bounds__(128) void pf_topk_kernel(PrefillArgs a, const double *logits, uint32_t *topk_idx) {
   __shared__ double lg[kMaxExperts];
   __shared__ uint32_t k32[kMaxExperts];
   __shared__ int sel[kMaxTopK];
   __shared__ double selv[kMaxTopK];
-  __shared__ uint32_t prev;
-  __shared__ int all_sel[kTok * kMaxTopK];
-  __shared__ int cnt[kMaxExperts + 1];
-  __shared__ uint32_t emask[kMaxExperts];
-  __shared__ int wsum[2];
-  __shared__ int sjx[kMaxExperts];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int E = a.n_experts, k = a.top_k, t = a.t;
+  const int E = a.n_experts, k = a.top_k;
   const int r = blockIdx.x;
   const int Ep = (E + 7) & ~7;
-  // the descriptors of experts threadIdx.x and threadIdx.x + 128, for the
-  // sub-job records in case this block is the last (loaded with the logits,
-  // so that the last block does not wait for them)
-  const uint64_t rv0 = a.rec[min(int(threadIdx.x), E - 1)];
-  const uint64_t rv1 = a.rec[min(int(threadIdx.x) + 128, E - 1)];
   // logits (+ 0.0 folds -0 into +0, so equal values tie on the id alone) and
   // 32-bit order keys of them rounded to float32; padding keys are 0, below
   // every logit's key
@@ -230,85 +219,6 @@ __global__ __launch_bounds__(128) void pf_topk_kernel(PrefillArgs a, const doubl
       a.topk_w[r * k + lane] = float(ex / sum);
     }
   }
-  block_signal(counter, 1u, &prev);
-  __syncthreads();
-  if (prev != uint32_t(t - 1)) return;
-  // last block: rows grouped by expert, experts ascending, rows ascending.
-  // Each expert gets a mask of the rows that selected it (a row selects an
-  // expert at most once, t <= 32); an entry's place is the expert's start
-  // plus the rows below it in that mask.
-  for (int p = threadIdx.x; p < t * k; p += 128) all_sel[p] = int(ld_dev(topk_idx + p));
-  for (int e = threadIdx.x; e < kMaxExperts; e += 128) emask[e] = 0u;
-  __syncthreads();
-  for (int p = threadIdx.x; p < t * k; p += 128) atomicOr(&emask[all_sel[p]], 1u << (p / k));
-  __syncthreads();
-  // exclusive scan over experts of (rows << 20 | heavy << 10 | light), two
-  // experts a thread: an expert with more than 8 rows is heavy (one
-  // sub-job, two above 16 rows: sub-jobs hold at most 16 rows), one with 1-8
-  // rows light
-  {
-    const int e0 = 2 * threadIdx.x, e1 = e0 + 1;
-    const int c0 = e0 < E ? __popc(emask[e0]) : 0, c1 = e1 < E ? __popc(emask[e1]) : 0;
-    const int v0 = (c0 << 20) | ((c0 > 8 ? 1 + int(c0 > 16) : 0) << 10) | int(c0 > 0 && c0 <= 8);
-    const int v1 = (c1 << 20) | ((c1 > 8 ? 1 + int(c1 > 16) : 0) << 10) | int(c1 > 0 && c1 <= 8);
-    int incl = v0 + v1;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += o;
-    }
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    const int excl = incl - (v0 + v1) + (wave ? wsum[0] : 0);
-    if (e0 < E) { cnt[e0] = excl; }
-    if (e1 < E) { cnt[e1] = excl + v0; }
-    if (threadIdx.x == 0) cnt[E] = wsum[0] + wsum[1];
-  }
-  __syncthreads();
-  // sub-jobs (at most 16 rows each), longest first: the shared expert's,
-  // then the heavy experts', then the light ones' (experts ascending in
-  // each), so that the items with the most rounds start their loads first.
-  // Each gets a record: expert, first entry and rows, descriptor, and the
-  // token row of each slot (written with the entries below), so that a work
-  // item finds all it needs in one load.
-  const int n_shared = t > 16 ? 2 : 1, n_heavy = (cnt[E] >> 10) & 1023;
-  auto job_rec = [&](int sj, int e, int base, int m, uint64_t d) {
-    int32_t *jr = a.meta + kJobInts * (1 + sj);
-    jr[0] = e;
-    jr[1] = base | (m << 16);
-    jr[2] = int32_t(uint32_t(d));
-    jr[3] = int32_t(uint32_t(d >> 32));
-  };
-  for (int e = threadIdx.x; e <= E; e += 128) {
-    const int v = cnt[e];
-    expert_ptr[e] = v >> 20;
-    if (e < E && emask[e]) {
-      const int c = __popc(emask[e]);
-      const int sj = c > 8 ? n_shared + ((v >> 10) & 1023) : n_shared + n_heavy + (v & 1023);
-      const uint64_t d = e == int(threadIdx.x) ? rv0 : rv1;
-      sjx[e] = sj;
-      job_rec(sj, e, v >> 20, min(c, 16), d);
-      if (c > 16) job_rec(sj + 1, e, (v >> 20) + 16, c - 16, d);
-    }
-  }
-  if (threadIdx.x == 0) {
-    for (int h = 0; h < n_shared; ++h) {
-      job_rec(h, -1, t * k + 16 * h, min(t - 16 * h, 16), a.shared_rec);
-      uint32_t *rows = reinterpret_cast<uint32_t *>(a.meta + kJobInts * (1 + h) + 4);
-      for (int i = 0; i < 4; ++i)
-        rows[i] = uint32_t(16 * h + 4 * i) * 0x01010101u + 0x03020100u;
-    }
-    a.meta[0] = n_shared + n_heavy + (cnt[E] & 1023);
-  }
-  __syncthreads();
-  for (int p = threadIdx.x; p < t * k; p += 128) {
-    const int e = all_sel[p], r = p / k;
-    const int q = __popc(emask[e] & ((1u << r) - 1u)), pos = (cnt[e] >> 20) + q;
-    entry_row[pos] = r;
-    entry_rank[pos] = p - r * k;
-    reinterpret_cast<uint8_t *>(a.meta + kJobInts * (1 + sjx[e] + (q >> 4)) + 4)[q & 15] = uint8_t(r);
-  }
-  if (threadIdx.x == 0) st_dev(counter, 0u);
 }
 
 // --------------------------------------------------------- shared helpers
@@ -410,6 +320,136 @@ struct Job {
   uint64_t desc;
   int lane_row;       // lane n < m: token row of slot n
 };
+
+// Rows grouped by expert (experts ascending, rows ascending inside an
+// expert) and the sub-jobs (at most 16 rows of one expert), longest first:
+// the shared expert's, then those of experts with more than 8 rows, then
+// the rest, experts ascending in each, so that the items with the most
+// rounds issue their loads first.  Every gate/up block builds it in LDS from
+// the top-k ids and the descriptors (one load each), so that no pass needs a
+// cross-block step for it; one block writes the entry order (CSR) and the
+// sub-job records for the down pass.
+struct Grouping {
+  uint32_t emask[kMaxExperts];   // rows that selected the expert (a row selects an expert once, t <= 32)
+  int scan[kMaxExperts];         // exclusive scan of (rows << 20 | heavy << 10 | light) over experts
+  uint64_t desc[kMaxExperts];
+  int job[2 * kMaxExperts + 2];  // sub-job -> expert | (half << 16), or -1 - half for the shared expert
+  int wsum[kWaves];
+};
+
+// position of the i-th (from 0) set bit of m (m has more than i)
+__device__ inline int nth_set_bit(uint32_t m, int i) {
+  int pos = 0;
+#pragma unroll
+  for (int s = 16; s >= 1; s >>= 1)
+    if (__popc(m & ((1u << (pos + s)) - 1u)) <= i) pos += s;
+  return pos;
+}
+
+// Builds the grouping; returns the sub-job count.  All threads call it.
+__device__ inline int build_grouping(const PrefillArgs &a, Grouping &gr) {
+  static_assert(kThreads == kMaxExperts, "one thread per expert");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.n_experts, k = a.top_k, t = a.t, nsel = t * k;   // nsel <= 2 kThreads
+  const uint32_t s0 = a.topk_idx[min(tid, nsel - 1)], s1 = a.topk_idx[min(tid + kThreads, nsel - 1)];
+  const uint64_t rv = a.rec[min(tid, E - 1)];
+  gr.emask[tid] = 0u;
+  __syncthreads();
+  if (tid < nsel) atomicOr(&gr.emask[s0], 1u << (tid / k));
+  if (tid + kThreads < nsel) atomicOr(&gr.emask[s1], 1u << ((tid + kThreads) / k));
+  __syncthreads();
+  // an expert with more than 8 rows is heavy (one sub-job, two above 16
+  // rows), one with 1-8 rows light
+  const int c = tid < E ? __popc(gr.emask[tid]) : 0;
+  const int val = (c << 20) | ((c > 8 ? 1 + int(c > 16) : 0) << 10) | int(c > 0 && c <= 8);
+  int incl = val;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) gr.wsum[wave] = incl;
+  __syncthreads();
+  int pre = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) pre += w < wave ? gr.wsum[w] : 0;
+  const int total = (gr.wsum[0] + gr.wsum[1]) + (gr.wsum[2] + gr.wsum[3]);
+  const int excl = incl - val + pre;
+  const int n_shared = t > 16 ? 2 : 1, n_heavy = (total >> 10) & 1023;
+  gr.scan[tid] = excl;
+  gr.desc[tid] = rv;
+  if (c > 0) {
+    const int sj = c > 8 ? n_shared + ((excl >> 10) & 1023) : n_shared + n_heavy + (excl & 1023);
+    gr.job[sj] = tid;
+    if (c > 16) gr.job[sj + 1] = tid | (1 << 16);
+  }
+  if (tid < n_shared) gr.job[tid] = -1 - tid;
+  __syncthreads();
+  return n_shared + n_heavy + (total & 1023);
+}
+
+// Sub-job sj of the grouping; lane_row = the token row of slot lane & 15.
+__device__ inline Job job_from(const PrefillArgs &a, const Grouping &gr, int sj) {
+  const int n = threadIdx.x & 15;
+  const int je = __builtin_amdgcn_readfirstlane(gr.job[sj]);
+  Job j;
+  if (je < 0) {
+    const int h = -1 - je;
+    j.e = -1;
+    j.base = a.t * a.top_k + 16 * h;
+    j.m = min(16, a.t - 16 * h);
+    j.desc = a.shared_rec;
+    j.lane_row = 16 * h + min(n, j.m - 1);
+  } else {
+    const int e = je & 0xffff, h = je >> 16;
+    const uint32_t em = __builtin_amdgcn_readfirstlane(gr.emask[e]);
+    j.e = e;
+    j.base = (__builtin_amdgcn_readfirstlane(gr.scan[e]) >> 20) + 16 * h;
+    j.m = min(16, __popc(em) - 16 * h);
+    const uint64_t d = gr.desc[e];
+    j.desc = uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(d)))) |
+             (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(d >> 32)))) << 32);
+    j.lane_row = nth_set_bit(em, 16 * h + min(n, j.m - 1));
+  }
+  return j;
+}
+
+// The entry order (CSR: expert starts, each entry's row and rank) and the
+// sub-job records of the down pass, from one block's grouping.
+__device__ inline void write_grouping(const PrefillArgs &a, const Grouping &gr, int n_jobs) {
+  const int tid = threadIdx.x;
+  const int E = a.n_experts, k = a.top_k, t = a.t;
+  for (int e = tid; e <= E; e += kThreads)
+    a.expert_ptr[e] = e < E ? gr.scan[e] >> 20 : t * k;
+  for (int p = tid; p < t * k; p += kThreads) {
+    const int e = int(a.topk_idx[p]), r = p / k;
+    const int pos = (gr.scan[e] >> 20) + __popc(gr.emask[e] & ((1u << r) - 1u));
+    a.entry_row[pos] = r;
+    a.entry_rank[pos] = p - r * k;
+  }
+  for (int sj = tid; sj < n_jobs; sj += kThreads) {
+    const int je = gr.job[sj];
+    int32_t *jr = a.meta + kJobInts * (1 + sj);
+    int e, base, m;
+    uint64_t d;
+    if (je < 0) {
+      e = -1;
+      base = t * k + 16 * (-1 - je);
+      m = min(16, t - 16 * (-1 - je));
+      d = a.shared_rec;
+    } else {
+      e = je & 0xffff;
+      base = (gr.scan[e] >> 20) + 16 * (je >> 16);
+      m = min(16, __popc(gr.emask[e]) - 16 * (je >> 16));
+      d = gr.desc[e];
+    }
+    jr[0] = e;
+    jr[1] = base | (m << 16);
+    jr[2] = int32_t(uint32_t(d));
+    jr[3] = int32_t(uint32_t(d >> 32));
+  }
+  if (tid == 0) a.meta[0] = n_jobs;
+}
 
 // the record of sub-job sj (below the workspace's capacity of sub-jobs)
 __device__ inline Job job_of(const PrefillArgs &a, int sj) {
@@ -821,16 +861,16 @@ __device__ __forceinline__ void mfma_tile_down(const TileSrc &src, DownBuf &buf,
 // term.
 __global__ __launch_bounds__(kThreads, 3) void pf_gate_up_kernel(PrefillArgs a) {
   __shared__ TileBuf buf;
+  __shared__ Grouping gr;
   __shared__ float red[kWaves][16];
   const int H = a.hidden, I = a.inter;
-  // grid: (tile, sub-job); the first item's record loads with the sub-job
-  // count (gridDim.y never exceeds the records the workspace holds)
+  // grid: (tile, sub-job)
   const int tile = blockIdx.x;
-  const int n_jobs = a.meta[0];
-  Job j = job_of(a, blockIdx.y);
+  const int n_jobs = build_grouping(a, gr);
+  if (blockIdx.x == 0 && blockIdx.y == 0) write_grouping(a, gr, n_jobs);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, nl = lane & 15;
   for (int sj = blockIdx.y; sj < n_jobs; sj += gridDim.y) {
-    if (sj != int(blockIdx.y)) j = job_of(a, sj);
+    const Job j = job_from(a, gr, sj);
     const bool ok = record_ok(j.desc, a.pool_bytes, H, I);
     const int bits = ok ? bits_of_tag(j.desc) : 4, order = bits == 4 ? 0 : 1;
     floatx4 acc = {0, 0, 0, 0};
@@ -997,8 +1037,7 @@ hipError_t launch_prefill(const PrefillArgs &a, const uint16_t *router, const ui
   hipLaunchKernelGGL(pf_router_kernel, dim3(route_blocks), dim3(kThreads), 0, s, a, router, gvec,
                      logits, gamma);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(pf_topk_kernel, dim3(a.t), dim3(128), 0, s, a, logits, topk_idx, counter,
-                     expert_ptr, entry_row, entry_rank);
+  hipLaunchKernelGGL(pf_topk_kernel, dim3(a.t), dim3(128), 0, s, a, logits, topk_idx);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = mark(0)) != hipSuccess) return e;
   const int max_jobs = min(a.n_experts, a.t * a.top_k) + 1;
