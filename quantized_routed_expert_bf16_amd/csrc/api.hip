@@ -386,9 +386,7 @@ int moe_prefill_forward(const float *x, int32_t t, const moe_router *router, moe
   pa.status = reinterpret_cast<uint32_t *>(ws + L.counters) + kSyncStatus;
   pa.out = out;
   rc = launched(launch_prefill(pa, router->weight, shared->gate, plan->logits, plan->gamma,
-                               plan->topk_idx, reinterpret_cast<uint32_t *>(ws + L.counters) + kSyncRoute,
-                               plan->expert_ptr, plan->entry_row, plan->entry_rank, s, g_stage_ev,
-                               g_stage_n),
+                               plan->topk_idx, s, g_stage_ev, g_stage_n),
                 "prefill");
   return rc ? rc : ok();
 }

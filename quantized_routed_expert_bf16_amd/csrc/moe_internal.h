@@ -98,7 +98,6 @@ constexpr int kSyncSliceStride = 64;        // slice x owns words [64x, 64x + 64
 constexpr int kSliceRoute = 0;              //   router blocks of the slice arrived
 constexpr int kSliceGu = 32;                //   gate/up units of the slice done
 constexpr int kSliceExit = 48;              //   blocks of the slice that left
-constexpr int kSyncRoute = 512;             // prefill top-k kernel: blocks arrived
 constexpr int kSyncStatus = 520;            // bit 0: bad descriptor skipped; bit 2: a wait ran out
 constexpr int kSyncExit = 528;              // slices whose blocks all left
 constexpr int kSyncAbort = 576;             // set when a wait ran out: all waits fall through
@@ -140,9 +139,8 @@ struct PrefillArgs {
   float *out;                  // [t][H]
 };
 hipError_t launch_prefill(const PrefillArgs &a, const uint16_t *router, const uint16_t *gvec,
-                          double *logits, float *gamma, uint32_t *topk_idx, uint32_t *counter,
-                          int32_t *expert_ptr, int32_t *entry_row, int32_t *entry_rank,
-                          hipStream_t s, hipEvent_t *stage_ev, int n_ev);
+                          double *logits, float *gamma, uint32_t *topk_idx, hipStream_t s,
+                          hipEvent_t *stage_ev, int n_ev);
 
 
 }  // namespace moe

@@ -11,11 +11,12 @@
 // Kernels (one stream, in order):
 //   P1 router logits (float64) of the t rows and, for the experts, an f16
 //      hi/lo split of x plus per-64 group sums of x;
-//   P2 per-row top-k and weights; the last block groups the rows by expert
-//      (experts ascending, rows ascending) and lists the sub-jobs (at most
-//      16 rows of one expert), longest first, one record each (expert,
-//      entries, descriptor, token rows) that a work item reads in one load;
-//   P3 gate/up: per (used expert, 64 gate/up rows), MFMA 16x16x32 f16 tiles
+//   P2 per-row top-k and weights (one block a row, nothing across blocks);
+//   P3 gate/up: every block first groups the rows by expert from the top-k
+//      ids (experts ascending, rows ascending) and lists the sub-jobs (at
+//      most 16 rows of one expert), longest first; one block also writes the
+//      entry order and one record per sub-job (expert, entries, descriptor)
+//      for P4; then per (used expert, 64 gate/up rows), MFMA 16x16x32 f16 tiles
 //      of 16 rows x 16 tokens (1 or 2 token tiles for m <= 16 or <= 32);
 //   P4 down: per (used expert, 64 output rows), same tiles, writes the
 //      routing-weighted rows of every (row, rank) entry;
@@ -1024,9 +1025,8 @@ __global__ __launch_bounds__(kCombineThreads) void pf_combine_kernel(PrefillArgs
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &a, const uint16_t *router, const uint16_t *gvec,
-                          double *logits, float *gamma, uint32_t *topk_idx, uint32_t *counter,
-                          int32_t *expert_ptr, int32_t *entry_row, int32_t *entry_rank,
-                          hipStream_t s, hipEvent_t *stage_ev, int n_ev) {
+                          double *logits, float *gamma, uint32_t *topk_idx, hipStream_t s,
+                          hipEvent_t *stage_ev, int n_ev) {
   auto mark = [&](int i) -> hipError_t {
     if (i < n_ev && stage_ev[i]) return hipEventRecord(stage_ev[i], s);
     return hipSuccess;
