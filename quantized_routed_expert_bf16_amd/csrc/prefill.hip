@@ -361,21 +361,29 @@ __device__ inline int build_grouping(const PrefillArgs &a, Grouping &gr) {
   __syncthreads();
   // an expert with more than 8 rows is heavy (one sub-job, two above 16
   // rows), one with 1-8 rows light
+  // The scan inside a wave is bit-sliced: each field is a sum of bits times
+  // their weights, and a bit's prefix over the lanes is a ballot counted
+  // below the lane (no lane exchanges).
   const int c = tid < E ? __popc(gr.emask[tid]) : 0;
-  const int val = (c << 20) | ((c > 8 ? 1 + int(c > 16) : 0) << 10) | int(c > 0 && c <= 8);
-  int incl = val;
+  const int hv = c > 8 ? 1 + int(c > 16) : 0, lt = int(c > 0 && c <= 8);
+  int wexcl = 0, wtot = 0;
+  auto slice = [&](bool bit, int weight) {
+    const uint64_t m = __ballot(bit);
+    wexcl += weight * int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
+    wtot += weight * __popcll(m);
+  };
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += o;
-  }
-  if (lane == 63) gr.wsum[wave] = incl;
+  for (int b = 0; b < 6; ++b) slice((c >> b) & 1, 1 << (20 + b));   // c <= 32
+  slice(hv & 1, 1 << 10);
+  slice(hv >> 1, 2 << 10);
+  slice(lt, 1);
+  if (lane == 0) gr.wsum[wave] = wtot;
   __syncthreads();
   int pre = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) pre += w < wave ? gr.wsum[w] : 0;
   const int total = (gr.wsum[0] + gr.wsum[1]) + (gr.wsum[2] + gr.wsum[3]);
-  const int excl = incl - val + pre;
+  const int excl = wexcl + pre;
   const int n_shared = t > 16 ? 2 : 1, n_heavy = (total >> 10) & 1023;
   gr.scan[tid] = excl;
   gr.desc[tid] = rv;
