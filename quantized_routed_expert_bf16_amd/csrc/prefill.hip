@@ -66,7 +66,7 @@ constexpr bool frag_maps_inverse() {
 static_assert(frag_maps_inverse(), "frag_pos must invert frag_code");
 
 // ------------------------------------------------------------------ P1
-constexpr int kRouteTok = 4;     // rows per router block
+constexpr int kRouteTok = 2;     // rows per router block
 constexpr int kRouteSteps = 4;   // 512-input steps a lane has in flight (all of them at H = 2048)
 
 __host__ __device__ inline int pf_router_blocks(int n_experts, int t) {
