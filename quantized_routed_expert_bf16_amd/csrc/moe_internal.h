@@ -17,7 +17,7 @@ constexpr int kSlotStride = MOE_SLOT_STRIDE;
 constexpr int kMaxNb = MOE_MAX_NB;
 constexpr int kSharedSlot = 63;   // act / partial index used for the shared expert
 constexpr int kMaxExperts = 256;
-constexpr int kJobInts = 8;   // prefill sub-job record (ints), after a header of the same size
+constexpr int kJobInts = 4;   // prefill sub-job record (ints), after a header of the same size
 constexpr int kMaxTopK = 15;
 
 // ----------------------------------------------------------- record layout
@@ -132,9 +132,9 @@ struct PrefillArgs {
   float *asum;                 // [act_rows][I/32] sums of act over 32-column blocks
   int act_rows;                // entries the act buffer holds (shared entries last)
   float *y;                    // [t][k+1][H] weighted output per (row, rank); rank k = shared
-  int32_t *meta;               // [0] sub-job count; sub-job s at 8 + 8 s: expert (-1 = shared),
-                               // first entry | rows << 16, descriptor, token row of each slot
-                               // (bytes); written by the gate/up pass for the down pass
+  int32_t *meta;               // [0] sub-job count; sub-job s at 4 + 4 s: expert (-1 = shared),
+                               // first entry | rows << 16, descriptor (two words); written by
+                               // the gate/up pass for the down pass
   uint32_t *status;
   float *out;                  // [t][H]
 };

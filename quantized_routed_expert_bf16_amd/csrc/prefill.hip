@@ -319,7 +319,7 @@ struct Job {
   int base;     // first entry index of its rows
   int m;        // rows (1..16)
   uint64_t desc;
-  int lane_row;       // lane n < m: token row of slot n
+  int lane_row;       // lane n < m: token row of slot n (set by the gate/up pass's grouping)
 };
 
 // Rows grouped by expert (experts ascending, rows ascending inside an
@@ -462,8 +462,8 @@ __device__ inline void write_grouping(const PrefillArgs &a, const Grouping &gr, 
 
 // the record of sub-job sj (below the workspace's capacity of sub-jobs)
 __device__ inline Job job_of(const PrefillArgs &a, int sj) {
-  typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
-  const i32x8 r = *reinterpret_cast<const i32x8 *>(a.meta + kJobInts * (1 + sj));
+  typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+  const i32x4 r = *reinterpret_cast<const i32x4 *>(a.meta + kJobInts * (1 + sj));
   Job j;
   j.e = __builtin_amdgcn_readfirstlane(r[0]);
   const int bm = __builtin_amdgcn_readfirstlane(r[1]);
@@ -471,11 +471,7 @@ __device__ inline Job job_of(const PrefillArgs &a, int sj) {
   j.m = bm >> 16;
   j.desc = uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(r[2]))) |
            (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(r[3]))) << 32);
-  // byte n of words 4..7 (slots past the job's rows hold stale bytes, never used)
-  const int n = threadIdx.x & 15;
-  const uint32_t w01 = (n & 4) ? uint32_t(r[5]) : uint32_t(r[4]);
-  const uint32_t w23 = (n & 4) ? uint32_t(r[7]) : uint32_t(r[6]);
-  j.lane_row = int((((n & 8) ? w23 : w01) >> (8 * (n & 3))) & 255u);
+  j.lane_row = -1;   // the down pass's B rows are the job's act rows
   return j;
 }
 
