@@ -956,6 +956,34 @@ __device__ __forceinline__ void gate_up_item(const LayerArgs &a, int x, uint64_t
   }
 }
 
+// ----------------------------------------------------------------- exit
+// Two-level exit count: a block counts itself out of its slice once it has
+// made its last use of the counters (every block has read the call's epoch
+// by then); the last block of a slice counts the slice out, and the last
+// slice's block puts the counters back to zero and publishes the epoch.  A
+// block whose last down tile it combines issues its slice-level count before
+// the combine (which waits on epoch-tagged partials, not on counters) and
+// reads the result after it: the count's round trip runs beside the combine.
+__device__ __forceinline__ uint32_t exit_count_issue(const LayerArgs &a, int x) {
+  __syncthreads();   // every thread is past its last counter use
+  return threadIdx.x == 0 ? __hip_atomic_fetch_add(sw(a, x, kSliceExit), 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                          : 0u;
+}
+template <int NB>
+__device__ __forceinline__ void exit_count_finish(const LayerArgs &a, Shared<NB> &sh, uint32_t prev) {
+  if (threadIdx.x == 0) sh.prev = prev;
+  __syncthreads();
+  if (sh.prev == uint32_t(a.per_slice - 1)) {
+    block_signal(a.l.sync + kSyncExit, 1u, &sh.prev);
+    __syncthreads();
+    if (sh.prev == uint32_t(kSlices - 1)) {   // every block has read the epoch: publish it
+      for (int i = threadIdx.x; i < kSyncWords; i += kThreads)
+        if (i != kSyncStatus) st_dev(a.l.sync + i, i == kSyncEpoch ? sh.ep : 0u);
+    }
+  }
+}
+
 // ----------------------------------------------------------------- down
 // The block of slice tile % slices sums the tile's rows of every slice's
 // partial in slice order (re-reading, boundedly, partials not yet of this
@@ -975,8 +1003,9 @@ __device__ __forceinline__ void combine_tile(const LayerArgs &a, const Shared<NB
 #pragma unroll
         for (int q = 0; q < kSlices; ++q) all &= q >= a.n_slices || uint32_t(w[q] >> 32) == sh.ep;
         if (all) break;
+        // (no abort flag from here: the counters may already be reset for the
+        // next call, which must not start aborted)
         if ((it & 63) == 0 && (ld_dev(a.l.sync + kSyncAbort) || it > kSpinLimit)) {
-          st_dev(a.l.sync + kSyncAbort, 1u);
           set_status(a, 4u);
           break;
         }
@@ -1057,11 +1086,12 @@ __device__ __forceinline__ void down_load(const LayerArgs &a, const Shared<NB> &
 }
 
 template <int NB>
-__device__ __forceinline__ void publish_partial(const LayerArgs &a, Shared<NB> &sh, int x, int tile, float (&acc)[NB]);
+__device__ __forceinline__ void publish_partial(const LayerArgs &a, Shared<NB> &sh, int x, int tile, float (&acc)[NB],
+                                                bool last);
 
 template <int NB>
 __device__ __forceinline__ void run_down(const LayerArgs &a, Shared<NB> &sh, int x, int tile, float *act_lds,
-                         float *asum_lds) {
+                         float *asum_lds, bool last) {
   const int lane = threadIdx.x & 63;
   const int I = a.l.inter, W = a.W;
   const int cpr = W / kChunk;                 // chunks per row in the slice (1..8)
@@ -1161,14 +1191,15 @@ __device__ __forceinline__ void run_down(const LayerArgs &a, Shared<NB> &sh, int
         acc[b] = fmaf(sh.wslot[b][slot], fmaf(sc, P[b], bi * asum_lds[(sl * NB + b) * cpr + c]), acc[b]);
     }
   }
-  publish_partial<NB>(a, sh, x, tile, acc);
+  publish_partial<NB>(a, sh, x, tile, acc, last);
 }
 
 // Sum the row's 8 lanes (chunks x slot groups) and publish the slice
 // partial, tagged with this call's epoch: no wait and no counter, the
 // combining block checks every partial's tag.  Then the tile's combine.
 template <int NB>
-__device__ __forceinline__ void publish_partial(const LayerArgs &a, Shared<NB> &sh, int x, int tile, float (&acc)[NB]) {
+__device__ __forceinline__ void publish_partial(const LayerArgs &a, Shared<NB> &sh, int x, int tile, float (&acc)[NB],
+                                                bool last) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = group8_sum(acc[b]);
@@ -1180,7 +1211,9 @@ __device__ __forceinline__ void publish_partial(const LayerArgs &a, Shared<NB> &
       st_dev(a.l.opart + (size_t(x) * kMaxNb + b) * H + row,
              (uint64_t(sh.ep) << 32) | __float_as_uint(acc[b]));
 
+  const uint32_t prev = last ? exit_count_issue(a, x) : 0u;
   combine_tile<NB>(a, sh, x, tile);
+  if (last) exit_count_finish<NB>(a, sh, prev);
 }
 
 // ------------------------------------------------------- down on MFMA
@@ -1195,7 +1228,7 @@ constexpr int kDownSlots = 8;   // slots per wave per batch (2 kDownSlots per bl
 
 template <int NB>
 __device__ __forceinline__ void run_down_m(const LayerArgs &a, Shared<NB> &sh, int x, int tile, uint4 *frag,
-                                           float *gsum, float *red) {
+                                           float *gsum, float *red, bool last) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int H = a.l.hidden, I = a.l.inter;
   const int q = lane >> 4, j = lane & 15;
@@ -1330,7 +1363,9 @@ __device__ __forceinline__ void run_down_m(const LayerArgs &a, Shared<NB> &sh, i
     st_dev(a.l.opart + (size_t(x) * kMaxNb + b) * H + tile * kRowsPerTile + rr,
            (uint64_t(sh.ep) << 32) | __float_as_uint(v));
   }
+  const uint32_t prev = last ? exit_count_issue(a, x) : 0u;
   combine_tile<NB>(a, sh, x, tile);
+  if (last) exit_count_finish<NB>(a, sh, prev);
 }
 
 // The nb rows of x into LDS, chunk-major (ChunkX), and their per-32 sums.
@@ -1433,6 +1468,7 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
 
   const int x = blockIdx.x % kSlices, lr = blockIdx.x / kSlices;
   const int P = a.per_slice;
+  bool counted = false;   // counted out of the slice with its last down tile
   // this call's epoch (tags the slice partials; never 0, the workspace's
   // initial tag) is read while x is staged (stage_x)
 
@@ -1542,11 +1578,17 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
         const int slot = i / a.ups;
         gate_up_item<NB, CPL, kM>(a, x, sh.desc[slot], slot, i - slot * a.ups, xs, xsum, xb, xg, red, sh.ep);
       }
-      for (; i < n_gu + a.tiles; i += P) run_down<NB>(a, sh, x, i - n_gu, act_lds, asum_lds);
+      for (; i < n_gu + a.tiles; i += P) {
+        counted = true;
+        run_down<NB>(a, sh, x, i - n_gu, act_lds, asum_lds, i + P >= n_gu + a.tiles);
+      }
     }
     if constexpr (kM) {
       const int n_gu = sh.u * a.ups;
-      for (; i < n_gu + a.tiles; i += P) run_down_m<NB>(a, sh, x, i - n_gu, xb, xg, red);
+      for (; i < n_gu + a.tiles; i += P) {
+        counted = true;
+        run_down_m<NB>(a, sh, x, i - n_gu, xb, xg, red, i + P >= n_gu + a.tiles);
+      }
     }
   } else if (threadIdx.x == 0) {
     // a block of a slice without columns (I < 8 * 32) still reads the call's
@@ -1555,17 +1597,9 @@ __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
     sh.ep = e ? e : 1u;
   }
 
-  // two-level exit count; the last block out resets the counters
-  block_signal(sw(a, x, kSliceExit), 1u, &sh.prev);
-  __syncthreads();
-  if (sh.prev == uint32_t(P - 1)) {
-    block_signal(a.l.sync + kSyncExit, 1u, &sh.prev);
-    __syncthreads();
-    if (sh.prev == uint32_t(kSlices - 1)) {   // every block has read the epoch: publish it
-      for (int i = threadIdx.x; i < kSyncWords; i += kThreads)
-        if (i != kSyncStatus) st_dev(a.l.sync + i, i == kSyncEpoch ? sh.ep : 0u);
-    }
-  }
+  // a block without down tiles counts itself out here (the others did
+  // with their last tile)
+  if (!counted) exit_count_finish<NB>(a, sh, exit_count_issue(a, x));
 }
 
 // moe_route: the routing steps of the layer kernel alone.  Every block is a
